@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X: chunked prefill tokens/s + decode state GB/s.
+
+A step is one pass over the whole hot path on synthetic inputs already
+resident in HBM:
+  * kda_fwd_chunked on the prefill workload (default: 4 sequences x 4096
+    tokens, H = 32, d_k = d_v = 128, bf16 q/k/v and o, fp32 g/beta, S0 = 0,
+    S_T written), and
+  * kda_decode_step on the decode workload (256 sequences x 64 heads,
+    d = 128, fp32 state updated in place).
+Each launch is bracketed by HIP events recorded on the stream it runs on.
+`value` is prefill tokens per second over the K timed launches; the decode
+state bandwidth and both roofline fractions ride along in the same line.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill|long_prefill|varlen]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix, published
+PROFILE_PMC = os.path.join(ROOT, "profiles", "kda_prefill_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_95_amd", "csrc", f)
+                  for f in ("kda_prefill.hip", "kda_device.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(tokens: int, H: int, dk: int, dv: int, n_seqs: int, s0: bool) -> int:
+    """Algorithmic HBM bytes of one prefill launch: q, k (bf16, d_k), v (bf16,
+    d_v), g (fp32, d_k), beta (fp32), o (bf16, d_v) per token-head, plus the
+    fp32 S_T write (and S0 read) per (sequence, head)."""
+    per_th = 2 * dk * 2 + 2 * dv + 4 * dk + 4 + 2 * dv
+    state = n_seqs * H * dk * dv * 4
+    return tokens * H * per_th + state * (2 if s0 else 1)
+
+
+def prefill_flops(tokens: int, H: int, dk: int, dv: int) -> int:
+    """Algorithmic flops at the 16-token tile: 6 d_k d_v + 16 (3 d_k + 2 d_v)
+    per token-head (state products + intra-tile products)."""
+    return tokens * H * (6 * dk * dv + 16 * (3 * dk + 2 * dv))
+
+
+def decode_bytes(N: int, H: int, dk: int, dv: int) -> tuple:
+    state = N * H * dk * dv * 4 * 2                    # read + write
+    other = N * H * (2 * dk * 2 + 2 * dv + 4 * dk + 4 + 2 * dv)
+    return state, state + other
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_alg_bytes: int):
+    """HBM bytes per prefill launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        with open(PROFILE_PMC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(threads: int):
+    """The fp64 C oracle on the whole prefill workload (4 sequences x 4096
+    tokens x 32 heads, d = 128; about 20 core-seconds), timed on the host."""
+    from oracle import clib
+    from synth import WORKLOADS, batch_inputs
+    wl = WORKLOADS["prefill"]
+    b = batch_inputs(wl)
+    tokens = int(b["cu_seqlens"][-1])
+    t0 = time.perf_counter()
+    _, _, used = clib.fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], None,
+                          want_o=True, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"fp64 C oracle (token-by-token, OpenMP over (sequence, head)) on the "
+                      f"whole prefill workload: {len(b['lengths'])} seqs x {wl.seqlen} tokens x "
+                      f"{wl.H} heads, d=128; {dt:.2f} s wall on {used} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "long_prefill", "varlen", "varlen_1m"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this KDA build runs on exactly one GPU (no sharding, no "
+              "collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from gated_delta_rule_95_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    import gated_delta_rule_95_amd as kda
+    from synth import WORKLOADS, batch_inputs, decode_batch_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (generated on the host, seeded) ----------------
+    wl = WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    b = batch_inputs(wl)
+    log(f"[bench] generated {args.workload}: {int(b['cu_seqlens'][-1])} tokens, "
+        f"{len(b['lengths'])} seqs in {time.perf_counter() - t0:.1f}s")
+    dt_in = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    P = {key: torch.from_numpy(b[key]).to(dev).to(dt_in) for key in ("q", "k", "v")}
+    P.update({key: torch.from_numpy(b[key]).to(dev) for key in ("g", "beta")})
+    S0 = torch.from_numpy(b["s0"]).to(dev) if "s0" in b else None
+    n_seqs = len(b["lengths"])
+    tokens = int(b["cu_seqlens"][-1])
+    equal = wl.seqlen is not None
+    cu = None if equal else torch.from_numpy(b["cu_seqlens"]).to(dev)
+    if equal:
+        shp = (n_seqs, wl.seqlen, wl.H)
+        P = {key: (t.view(*shp, -1) if t.dim() == 3 else t.view(*shp)) for key, t in P.items()}
+    o = torch.empty(P["v"].shape, dtype=dt_in, device=dev)
+    S_T = torch.empty((n_seqs, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+    del b
+
+    def run_prefill():
+        kda.kda_fwd_chunked(P["q"], P["k"], P["v"], P["g"], P["beta"], S0=S0, cu_seqlens=cu,
+                            o=o, S_T=S_T)
+
+    dec = None
+    if not args.no_decode:
+        dw = WORKLOADS["decode"]
+        d = decode_batch_inputs(dw)
+        dec = {key: torch.from_numpy(d[key]).to(dev).to(torch.bfloat16) for key in ("q", "k", "v")}
+        dec.update({key: torch.from_numpy(d[key]).to(dev) for key in ("g", "beta", "S")})
+        dec["o"] = torch.empty((dw.n_seqs, dw.H, dw.dv), dtype=torch.bfloat16, device=dev)
+        del d
+
+    def run_decode():
+        kda.kda_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], dec["S"],
+                            o=dec["o"])
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + written")
+        del src, dst
+
+    # ---------------- warmup ----------------
+    for _ in range(args.warmup):
+        run_prefill()
+        if dec:
+            run_decode()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup {args.warmup} done")
+
+    # ---------------- timed steps ----------------
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        run_prefill()
+        ev[i][1].record(stream)
+        if dec:
+            ev[i][2].record(stream)
+            run_decode()
+            ev[i][3].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    pf_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    dc_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) if dec else None
+    log(f"[bench] prefill ms: mean {pf_ms.mean():.4f} min {pf_ms.min():.4f} "
+        f"max {pf_ms.max():.4f}")
+
+    pf_s = float(pf_ms.mean()) / 1e3
+    alg_b = prefill_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs, S0 is not None)
+    alg_f = prefill_flops(tokens, wl.H, wl.dk, wl.dv)
+    achieved = alg_b / pf_s / 1e9
+    traffic = measured_traffic(alg_b)
+    out = {
+        "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, 1xMI355X, % roofline",
+        "value": tokens / pf_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {n_seqs} seqs x "
+                               f"{tokens // n_seqs if equal else 'varlen'} tokens, H={wl.H}, "
+                               f"d_k=d_v={wl.dk}, bf16 q/k/v/o, fp32 g/beta/state, "
+                               f"S0={'given' if S0 is not None else 'zero'}, S_T returned",
+                   "tokens": tokens, "n_seqs": n_seqs, "H": wl.H, "d_k": wl.dk, "d_v": wl.dv,
+                   "chunk": 16,
+                   "decode_workload": "256 seqs x 64 heads, d=128, fp32 state in place"
+                   if dec else None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "kda_prefill_kernel", "alg_bytes_per_launch": alg_b,
+                     "launch_ms": pf_s * 1e3,
+                     "mfma_tflops": alg_f / pf_s / 1e12,
+                     "mfma_frac": alg_f / pf_s / 1e12 / BF16_PEAK_TFLOPS},
+    }
+    if dec:
+        dw = WORKLOADS["decode"]
+        st_b, all_b = decode_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv)
+        dc_s = float(dc_ms.mean()) / 1e3
+        out["decode"] = {"state_GBps": st_b / dc_s / 1e9, "launch_ms": dc_s * 1e3,
+                         "tokens_per_s": dw.n_seqs / dc_s,
+                         "roofline": {"bound": "hbm", "achieved": all_b / dc_s / 1e9,
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": all_b / dc_s / 1e9 / HBM_PEAK_GBS,
+                                      "kernel": "kda_decode_kernel",
+                                      "alg_bytes_per_launch": all_b}}
+    if not args.no_cpu:
+        threads = min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+"""gated_delta_rule_95_amd -- Kimi Delta Attention (KDA) on MI355X.
+
+Thin Python front of libkda.so (C ABI: include/kda.h).  PyTorch supplies
+device memory and the current HIP stream; every step of KDA runs in the
+library's hand-written gfx950 kernels.  Names follow the C ABI:
+
+    kda_fwd_chunked(q, k, v, g, beta, S0=None, cu_seqlens=None, ...) -> (o, S_T)
+    kda_decode_step(q, k, v, g, beta, S, ...) -> o        (S updated in place)
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
+
+__all__ = ["kda_fwd_chunked", "kda_decode_step", "KDAError", "version", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def version() -> str:
+    return _lib.version()
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KDA_BF16
+    if t == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t}; KDA takes bfloat16 or float32 q/k/v")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def kda_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S0: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None,
+                    output_final_state: bool = True,
+                    o: Optional[torch.Tensor] = None,
+                    S_T: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill.
+
+    q, k : [B, T, H, d_k] or packed [N, H, d_k] (bf16 or fp32); v : [..., H, d_v]
+    g    : [..., H, d_k] fp32 log-decay in [-5, 0];  beta : [..., H] fp32
+    S0   : [n_seqs, H, d_k, d_v] fp32 or None
+    cu_seqlens : int32 [n_seqs + 1] on the device (packed input only)
+    Returns (o [same leading shape, d_v], S_T [n_seqs, H, d_k, d_v] or None).
+    """
+    dev = q.device
+    if q.dim() == 4:
+        if cu_seqlens is not None and q.shape[0] != 1:
+            raise ValueError("cu_seqlens needs packed input ([N, H, d] or [1, N, H, d])")
+        lead = tuple(q.shape[:2])
+        n_seqs = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        N = q.shape[0] * q.shape[1]
+        H, dk = q.shape[2], q.shape[3]
+    elif q.dim() == 3:
+        lead = (q.shape[0],)
+        N, H, dk = q.shape
+        if cu_seqlens is None:
+            n_seqs = 1
+        else:
+            n_seqs = cu_seqlens.numel() - 1
+    else:
+        raise ValueError("q must be [B, T, H, d_k] or [N, H, d_k]")
+    dv = v.shape[-1]
+    _need(q, "q", device=dev)
+    _need(k, "k", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(v, "v", dtype=q.dtype, shape=lead + (H, dv), device=dev)
+    _need(g, "g", dtype=torch.float32, shape=lead + (H, dk), device=dev)
+    _need(beta, "beta", dtype=torch.float32, shape=lead + (H,), device=dev)
+    if S0 is not None:
+        _need(S0, "S0", dtype=torch.float32, shape=(n_seqs, H, dk, dv), device=dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+    in_dt = _dt(q.dtype)
+    od = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty(lead + (H, dv), dtype=od, device=dev)
+    else:
+        _need(o, "o", dtype=od, shape=lead + (H, dv), device=dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", dtype=torch.float32, shape=(n_seqs, H, dk, dv), device=dev)
+    lib = _lib.load()
+    st = lib.kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                             _ptr(cu_seqlens), n_seqs, N, H, dk, dv, in_dt, _dt(od),
+                             _ptr(o), _ptr(S_T), _stream(dev))
+    _lib.check(st)
+    return o, S_T
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor,
+                    out_dtype: Optional[torch.dtype] = None,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token per sequence.  q, k, g : [N, H, d_k]; v : [N, H, d_v];
+    beta : [N, H]; S : [N, H, d_k, d_v] fp32, updated in place.  Returns o."""
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", device=dev)
+    _need(k, "k", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(v, "v", dtype=q.dtype, shape=(N, H, dv), device=dev)
+    _need(g, "g", dtype=torch.float32, shape=(N, H, dk), device=dev)
+    _need(beta, "beta", dtype=torch.float32, shape=(N, H), device=dev)
+    _need(S, "S", dtype=torch.float32, shape=(N, H, dk, dv), device=dev)
+    od = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=od, device=dev)
+    else:
+        _need(o, "o", dtype=od, shape=(N, H, dv), device=dev)
+    lib = _lib.load()
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                             N, H, dk, dv, _dt(q.dtype), _dt(od), _ptr(o), _stream(dev))
+    _lib.check(st)
+    return o

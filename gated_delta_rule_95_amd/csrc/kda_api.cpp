@@ -1,0 +1,199 @@
+// C-ABI layer of libkda: argument validation, dtype/shape dispatch, errors.
+// Declarations and the contract of every entry point are in include/kda.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+#define KDA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+kda_status ok()
+{
+    g_err[0] = '\0';
+    return KDA_OK;
+}
+
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kda_status check_dtypes(kda_dtype in, kda_dtype out)
+{
+    if (in != KDA_F32 && in != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARG, "in_dtype %d is not a kda_dtype", (int)in);
+    if (out != KDA_F32 && out != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARG, "out_dtype %d is not a kda_dtype", (int)out);
+    if (in == KDA_F32 && out == KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "fp32 inputs with a bf16 output are not supported");
+    return KDA_OK;
+}
+
+kda_status check_dims(int32_t H, int32_t d_k, int32_t d_v)
+{
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1 (got %d)", H);
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v))
+        return fail(KDA_ERR_UNSUPPORTED, "d_k and d_v must be 16, 32, 64 or 128 (got %d, %d)",
+                    d_k, d_v);
+    return KDA_OK;
+}
+
+struct Ptr {
+    const void *p;
+    const char *name;
+    bool required;
+    size_t align;     // bytes: the widest vector access the kernels make
+};
+
+kda_status check_ptrs(const Ptr *ps, int n)
+{
+    for (int i = 0; i < n; ++i) {
+        if (!ps[i].p) {
+            if (ps[i].required) return fail(KDA_ERR_INVALID_ARG, "%s is NULL", ps[i].name);
+            continue;
+        }
+        if (!aligned(ps[i].p, ps[i].align))
+            return fail(KDA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", ps[i].name,
+                        ps[i].align);
+    }
+    return KDA_OK;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+    return x < y + nb && y < x + na;
+}
+
+kda_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t n_seqs,
+                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   float *S_T, kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
+    if ((s = check_dims(H, d_k, d_v)) != KDA_OK) return s;
+    if (n_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "n_seqs must be >= 0 (got %d)", n_seqs);
+    if (n_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens must be >= 0");
+    if (n_tokens >= (int64_t)1 << 31)
+        return fail(KDA_ERR_INVALID_ARG, "n_tokens must fit int32 (cu_seqlens is int32)");
+    if (n_seqs == 0) {
+        if (n_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens > 0 with n_seqs == 0");
+        return ok();
+    }
+    int32_t seqlen = 0;
+    if (!cu_seqlens) {
+        if (n_tokens % n_seqs)
+            return fail(KDA_ERR_INVALID_ARG,
+                        "without cu_seqlens n_tokens (%lld) must be a multiple of n_seqs (%d)",
+                        (long long)n_tokens, n_seqs);
+        seqlen = (int32_t)(n_tokens / n_seqs);
+    } else if (!aligned(cu_seqlens, 4)) {
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+    }
+    const bool have_tokens = n_tokens > 0;
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
+    const Ptr ps[] = {{q, "q", have_tokens, 2 * in_b}, {k, "k", have_tokens, 2 * in_b},
+                      {v, "v", have_tokens, 4 * in_b}, {g, "g", have_tokens, 8},
+                      {beta, "beta", have_tokens, 4}, {o, "o", have_tokens, 4 * out_b},
+                      {S0, "S0", false, 4}, {S_T, "S_T", false, 4}};
+    if ((s = check_ptrs(ps, 8)) != KDA_OK) return s;
+    const size_t o_bytes = (size_t)n_tokens * H * d_v * out_b;
+    const size_t st_bytes = (size_t)n_seqs * H * d_k * d_v * 4;
+    const void *ins[] = {q, k, v, g, beta, S0};
+    const size_t in_sz[] = {(size_t)n_tokens * H * d_k * in_b, (size_t)n_tokens * H * d_k * in_b,
+                            (size_t)n_tokens * H * d_v * in_b, (size_t)n_tokens * H * d_k * 4,
+                            (size_t)n_tokens * H * 4, st_bytes};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(o, o_bytes, ins[i], in_sz[i]) || overlap(S_T, st_bytes, ins[i], in_sz[i]))
+            return fail(KDA_ERR_INVALID_ARG, "an output buffer overlaps an input buffer");
+    }
+    if (overlap(o, o_bytes, S_T, st_bytes))
+        return fail(KDA_ERR_INVALID_ARG, "o overlaps S_T");
+
+    kda::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0;
+    a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs; a.n_tokens = n_tokens; a.seqlen = seqlen;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.o = o; a.S_T = S_T; a.stream = stream;
+    return hip_status(kda::launch_prefill(a), "kda_fwd_chunked launch");
+}
+
+KDA_API kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, float *S,
+                                   int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
+    if ((s = check_dims(H, d_k, d_v)) != KDA_OK) return s;
+    if (N < 0) return fail(KDA_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+    if (N == 0) return ok();
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
+    const Ptr ps[] = {{q, "q", true, in_b}, {k, "k", true, in_b}, {v, "v", true, 4 * in_b},
+                      {g, "g", true, 4}, {beta, "beta", true, 4}, {S, "S", true, 16},
+                      {o, "o", true, 4 * out_b}};
+    if ((s = check_ptrs(ps, 7)) != KDA_OK) return s;
+    const size_t nh = (size_t)N * H;
+    const size_t s_bytes = nh * d_k * d_v * 4;
+    const void *others[] = {q, k, v, g, beta, o};
+    const size_t sz[] = {nh * d_k * in_b, nh * d_k * in_b, nh * d_v * in_b, nh * d_k * 4,
+                         nh * 4, nh * d_v * out_b};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(S, s_bytes, others[i], sz[i]))
+            return fail(KDA_ERR_INVALID_ARG, "S overlaps another argument");
+    for (int i = 0; i < 5; ++i)
+        if (overlap(o, sz[5], others[i], sz[i]))
+            return fail(KDA_ERR_INVALID_ARG, "o overlaps an input");
+
+    kda::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o;
+    a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.stream = stream;
+    return hip_status(kda::launch_decode(a), "kda_decode_step launch");
+}
+
+KDA_API const char *kda_status_string(kda_status s)
+{
+    switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+KDA_API const char *kda_last_error(void) { return g_err; }
+
+KDA_API const char *kda_version(void) { return "0.1 gfx950"; }

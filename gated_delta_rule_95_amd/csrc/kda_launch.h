@@ -1,0 +1,37 @@
+// Internal launch interface between the C-ABI layer (kda_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *S;
+    void *o;
+    int32_t N, H, d_k, d_v;
+    bool in_bf16, out_bf16;
+    void *stream;
+};
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta, *S0;
+    const int32_t *cu_seqlens;   // nullptr: equal lengths seqlen
+    int32_t n_seqs;
+    int64_t n_tokens;
+    int32_t seqlen;              // used when cu_seqlens == nullptr
+    int32_t H, d_k, d_v;
+    bool in_bf16, out_bf16;
+    void *o;
+    float *S_T;
+    void *stream;
+};
+
+hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_prefill(const PrefillArgs &a);
+
+}  // namespace kda

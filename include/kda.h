@@ -1,0 +1,162 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes; no C++ or framework types cross it.
+ *
+ * What is computed.  Per head, KDA keeps a d_k x d_v state S whose rows are
+ * key channels and, for every token t, applies
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                               alpha_t = exp(g_t)
+ *
+ * (Kimi K3 architecture walkthrough, mhpq.cn/news/56770, section
+ * "KDA 到底在算什么": the state-update equation and, in its figure caption,
+ * the order decay -> erase along k_t -> write; the read uses the updated
+ * state.  alpha = exp(g) with g bounded below by -5: K3-on-TPU essay,
+ * blog.higcp.com, section "KDA + Gated MLA", lower-bounded decay.)
+ * No attention scale is applied to q.
+ *
+ * Layouts (all dense, row-major, token-major, no padding):
+ *     q, k    [n_tokens, H, d_k]      dtype = in_dtype
+ *     v       [n_tokens, H, d_v]      dtype = in_dtype
+ *     o       [n_tokens, H, d_v]      dtype = out_dtype
+ *     g       [n_tokens, H, d_k]      float32, natural-log decay, g in [-5, 0]
+ *     beta    [n_tokens, H]           float32, beta in [0, 1]
+ *     S0, S_T, S  [n_seqs, H, d_k, d_v]  float32, row = key channel
+ *     cu_seqlens  int32 [n_seqs + 1], cu_seqlens[0] = 0, non-decreasing,
+ *                 cu_seqlens[n_seqs] = n_tokens (device memory)
+ * The packed (varlen) layout follows the pages' description of a KDA
+ * implementation that packs variable-length sequences and keeps one
+ * recurrent state per sequence (K3-on-TPU essay, "KDA + Gated MLA" and the
+ * section on the existing TPU kernel).
+ *
+ * Alignment (bytes; the widest vector access the kernels make): q, k: two
+ * elements; v, o: four elements; g: 8 (prefill) / 4 (decode); beta, S0,
+ * S_T: 4; the decode state S: 16.  Any slice of a contiguous tensor along
+ * its token (or sequence) axis satisfies these.
+ *
+ * Ownership: the caller allocates every buffer in device memory (any HIP
+ * allocator) and keeps it alive until the work queued on `stream` is done.
+ * The library allocates no device memory, keeps no pointer after a call
+ * returns, and never synchronises the host.
+ *
+ * Errors: every entry point returns a kda_status; nothing aborts or throws
+ * across the ABI.  Argument problems are found on the host before anything
+ * is launched (nothing is written then).  A launch failure returns
+ * KDA_ERR_HIP.  kda_last_error() gives a message for the calling thread's
+ * most recent failure.  Values inside device buffers (cu_seqlens order, the
+ * range of g and beta) are preconditions that are NOT checked: g < -5 can
+ * overflow the bf16 rescale factors (the 16-token tile bound of the pages
+ * assumes g >= -5) and is undefined behaviour; a decreasing cu_seqlens
+ * yields unspecified output but stays within the buffers' bounds.
+ *
+ * Concurrency: calls are asynchronous on `stream` and re-entrant.  Calls
+ * that write the same buffers must be ordered by the caller.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION_MAJOR 0
+#define KDA_VERSION_MINOR 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer  */
+    KDA_ERR_UNSUPPORTED = 2, /* head size or dtype combination not built    */
+    KDA_ERR_HIP = 3          /* the HIP runtime reported an error           */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* Opaque stream handle: a hipStream_t (0 = the default stream). */
+typedef void *kda_stream_t;
+
+/*
+ * kda_fwd_chunked -- chunked prefill over a packed batch of sequences.
+ *
+ * For every sequence n (tokens cu_seqlens[n] .. cu_seqlens[n+1]-1) and head
+ * h, runs the recurrence above from S0[n, h] (zeros when S0 == NULL), writes
+ * o for every token and the final state to S_T[n, h] (skipped when
+ * S_T == NULL).  An empty sequence gives S_T[n] = S0[n] (or zeros).
+ * When cu_seqlens == NULL the batch is n_seqs sequences of equal length
+ * n_tokens / n_seqs laid out back to back ([B, T, H, d] == [B*T, H, d]);
+ * n_tokens must then be a multiple of n_seqs.
+ *
+ * The work is split into 16-token chunks (the decay tile of the pages: with
+ * g >= -5 a tile's cumulative log-decay stays in (-80, 0), so its rescale
+ * factors e^{+-80} fit bf16 and fp32).  Inside a chunk the WY/UT form
+ * (I + A)^{-1} Diag(beta) with A = strict_lower(Diag(beta) K~ K^T) is used;
+ * bf16 inputs run on bf16 matrix cores with fp32 accumulation (intra-chunk
+ * operands as bf16 hi/lo pairs), fp32 inputs on fp32 matrix cores.  The
+ * state is carried in fp32 between chunks.
+ *
+ * Arguments
+ *   q, k, v, g, beta   inputs, layouts above
+ *   S0                 float32 entry states or NULL
+ *   cu_seqlens         int32 device array or NULL (equal lengths)
+ *   n_seqs             number of sequences, >= 0 (0: nothing is done)
+ *   n_tokens           total tokens, >= 0
+ *   H                  heads, >= 1
+ *   d_k, d_v           16, 32, 64 or 128 each
+ *   in_dtype           KDA_BF16 or KDA_F32 (q, k, v)
+ *   out_dtype          dtype of o: KDA_BF16 (bf16 inputs only) or KDA_F32;
+ *                      fp32 o is exact fp32 accumulation before any rounding
+ *   o                  output (may be NULL iff n_tokens == 0)
+ *   S_T                float32 final states or NULL
+ *   stream             hipStream_t
+ */
+kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *S0,
+                           const int32_t *cu_seqlens, int32_t n_seqs,
+                           int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                           kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                           float *S_T, kda_stream_t stream);
+
+/*
+ * kda_decode_step -- one new token for each of N independent sequences.
+ *
+ * Applies the recurrence once per (sequence n, head h), updating
+ * S[n, h] (float32, [N, H, d_k, d_v]) IN PLACE, and writes o[n, h].  The
+ * in-place update is how the pages describe KDA decoding (K3-on-TPU essay,
+ * "KDA + Gated MLA", the costs section on speculative decoding).  The state
+ * is read once and written once; the step is bound by HBM bandwidth
+ * (the AI-accelerator checklist, lishengnan.com/aichip, "Decode: bandwidth
+ * roof first").
+ *
+ * Arguments
+ *   q, k      [N, H, d_k] in_dtype;  v [N, H, d_v] in_dtype
+ *   g         [N, H, d_k] float32;   beta [N, H] float32
+ *   S         [N, H, d_k, d_v] float32, read and overwritten
+ *   N, H      >= 0, >= 1;  d_k, d_v in {16, 32, 64, 128}
+ *   o         [N, H, d_v] out_dtype
+ * S must not overlap any other argument, nor o an input.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *S,
+                           int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                           kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                           kda_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *kda_status_string(kda_status s);
+
+/* Message for the calling thread's most recent failing call ("" if none). */
+const char *kda_last_error(void);
+
+/* "major.minor" plus the offload target the library was built for. */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,111 @@
+"""CPU tests of the C ABI: the library loads, exports exactly what
+include/kda.h declares, and rejects bad arguments with status codes before
+anything reaches the GPU (no compute call is made here)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from gated_delta_rule_95_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    declared = _lib.header_functions()
+    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_last_error",
+                        "kda_status_string", "kda_version"]
+    for name in declared:
+        assert hasattr(lib, name)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines()
+                       if " T " in ln and ln.split()[-1].startswith("kda_")})
+    assert exported == declared
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "KDA_OK"
+    assert _lib.status_string(1) == "KDA_ERR_INVALID_ARG"
+    assert _lib.status_string(2) == "KDA_ERR_UNSUPPORTED"
+    assert _lib.status_string(3) == "KDA_ERR_HIP"
+    assert "gfx950" in _lib.version()
+
+
+P = 0x10000   # a fake, suitably aligned address: never dereferenced, every
+              # call below fails validation before any launch
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P * 2, v=P * 3, g=P * 4, beta=P * 5, S0=None, cu=None, n_seqs=1,
+             n_tokens=16, H=1, dk=16, dv=16, ind=1, outd=1, o=P * 6, ST=None)
+    a.update(kw)
+    return lib.kda_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"],
+                               a["n_seqs"], a["n_tokens"], a["H"], a["dk"], a["dv"], a["ind"],
+                               a["outd"], a["o"], a["ST"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(beta=None), 1, "beta is NULL"),
+    (dict(o=None), 1, "o is NULL"),
+    (dict(dk=48), 2, "d_k"),
+    (dict(dv=256), 2, "d_k"),
+    (dict(H=0), 1, "H must be"),
+    (dict(n_seqs=-1), 1, "n_seqs"),
+    (dict(n_tokens=-5), 1, "n_tokens"),
+    (dict(n_seqs=3, n_tokens=16), 1, "multiple"),
+    (dict(ind=7), 1, "in_dtype"),
+    (dict(ind=0, outd=1), 2, "fp32 inputs"),
+    (dict(q=P + 2), 1, "aligned"),
+    (dict(v=P * 3 + 4), 1, "aligned"),
+    (dict(g=P * 4 + 4), 1, "aligned"),
+    (dict(cu=P + 2), 1, "cu_seqlens"),
+    (dict(n_seqs=0, n_tokens=5), 1, "n_seqs == 0"),
+    (dict(o=P * 2), 1, "overlaps"),
+    (dict(n_tokens=1 << 31, n_seqs=1), 1, "int32"),
+])
+def test_fwd_validation(lib, kw, status, msg):
+    assert fwd(lib, **kw) == status
+    assert msg in _lib.last_error()
+
+
+def test_fwd_nothing_to_do_is_ok(lib):
+    assert fwd(lib, n_seqs=0, n_tokens=0) == 0
+    assert _lib.last_error() == ""
+
+
+def dec(lib, **kw):
+    a = dict(q=P, k=P * 2, v=P * 3, g=P * 4, beta=P * 5, S=P * 64, N=2, H=2, dk=16, dv=16,
+             ind=1, outd=1, o=P * 7)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S"], a["N"],
+                               a["H"], a["dk"], a["dv"], a["ind"], a["outd"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(S=None), 1, "S is NULL"),
+    (dict(N=-1), 1, "N must be"),
+    (dict(dk=8), 2, "d_k"),
+    (dict(S=P), 1, "S overlaps"),
+    (dict(o=P), 1, "overlaps"),
+    (dict(g=P * 4 + 2), 1, "aligned"),
+    (dict(S=P * 64 + 8), 1, "aligned"),
+])
+def test_decode_validation(lib, kw, status, msg):
+    assert dec(lib, **kw) == status
+    assert msg in _lib.last_error()
+
+
+def test_decode_nothing_to_do_is_ok(lib):
+    assert dec(lib, N=0) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libkda.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()
