@@ -5,44 +5,52 @@
 // + b k v^T, o_t = S_t^T q_t, decay -> erase -> write) is evaluated 16 tokens
 // at a time.  16 is the decay tile of the pages: with the gate bounded below
 // by -5, the cumulative log-decay of 16 tokens stays inside (-80, 0], so the
-// rescale factors e^{+-Gc} of a tile are finite in bf16 and fp32 and every
-// intra-tile product can be a dense matrix product (K3-on-TPU essay,
-// blog.higcp.com, "KDA + Gated MLA", lower-bounded decay; the same section
-// of the K3 walkthrough).  For a chunk with entry state S and, per key
-// channel, the inclusive cumulative log-decay Gc_r from the chunk start:
+// rescale factors of a tile are finite in bf16 and fp32 and every intra-tile
+// product can be a dense matrix product (K3-on-TPU essay, blog.higcp.com,
+// "KDA + Gated MLA", lower-bounded decay; the lower-bounded-decay section of
+// the K3 walkthrough).
 //
-//   A  = strict_lower(Diag(beta) Kt Kh^T)   Kt = k e^{Gc}, Kh = k e^{-Gc}
-//   T  = (I + A)^{-1} Diag(beta)            (unit lower-triangular inverse)
-//   X  = V - Kt S,   U = T X
-//   O  = Qt S + P U, P = lower_incl(Qt Kh^T), Qt = q e^{Gc}
-//   S <- Diag(e^{Gc_16}) S + Kd^T U,        Kd = k e^{Gc_16 - Gc}
+// Chunk algebra (derived from the recurrence; the pages only sketch the
+// chunked form).  For a chunk of 16 tokens with entry state S and, per key
+// channel, the inclusive cumulative log-decay Gc_r from the chunk start, let
+// Gc_16 be the chunk total and reference every factor to the chunk END:
 //
-// which is the token recurrence rearranged (derived from it; the pages only
-// sketch the chunked form).
+//   E_r  = e^{Gc_r - Gc_16}  in [1, e^75]      Kd_r = k_r e^{Gc_16 - Gc_r}  (<= |k_r|)
+//   KE_r = k_r E_r,  QE_r = q_r E_r,            Sd = Diag(e^{Gc_16}) S   (the decayed state)
+//
+//   A  = strict_lower(Diag(beta) KE Kd^T),      P = lower_incl(QE Kd^T)
+//   T  = (I + A)^{-1} Diag(beta)                (unit lower-triangular inverse)
+//   X  = V - KE Sd,    U = T X
+//   O  = QE Sd + P U
+//   S' = Sd + Kd^T U
+//
+// since k_r e^{Gc_r} S = KE_r Sd and (k_r e^{Gc_r}).(k_i e^{-Gc_i}) = KE_r.Kd_i.
+// A term lost to underflow of Sd is below FLT_MIN e^75 (~4e-6) in absolute
+// value.
 //
 // Mapping.  One workgroup per (sequence, head, block of BV = 16 NW columns
-// of the state).  The columns of S evolve independently, so the d_v split
-// needs no communication.  The workgroup has NW consumer waves and one
-// helper wave:
-//  * consumer wave w keeps S[:, 16w : 16w+16] of its block in registers, in
-//    the 16x16 MFMA accumulator layout (lane l holds rows 4(l/16)+i,
-//    column l%16 of each 16x16 tile), and runs the S-dependent chain of
-//    chunk c;
-//  * the consumer waves together also build the decay-scaled operands of
-//    chunk c+2 (cumulative sums, exponentials, bf16 hi/lo splits) into LDS
-//    from registers loaded one chunk earlier;
+// of the state): the columns of S evolve independently, so the d_v split
+// needs no communication.  NW consumer waves and one helper wave:
+//  * consumer wave w keeps S[:, 16w : 16w+16] of its block in registers in
+//    the 16x16 MFMA accumulator layout (lane l holds rows 4(l/16)+i, column
+//    l%16 of each 16x16 tile) and runs the S-dependent chain of chunk c;
+//  * the consumer waves together build the operands of chunk c+NBUF-1
+//    (cumulative sums, exponentials, bf16 hi/lo splits) into LDS from
+//    registers loaded one chunk earlier;
 //  * the helper wave forms A and P of chunk c+1 on the matrix cores and
 //    inverts (I + A) by forward substitution in fp32.
-// Operands live in a three-deep LDS ring; one workgroup barrier per chunk.
+// NBUF = 3: one barrier per chunk (build c+2 | helper c+1 | consume c).
+// NBUF = 2: two barriers per chunk, a smaller LDS footprint (two workgroups
+// fit on one CU).
 //
 // Precision.  bf16 inputs: matrix-core operands are bf16 with fp32
 // accumulation; the state stays fp32 in registers.  Operands whose rounding
-// shows up in o or S (S itself, Qt, T, X, U, P, the Kh behind P, and Kd) are
-// kept as bf16 hi + lo pairs; only -Kt (in X and A) is a single bf16; a pair-by-pair product (h1 + l1)(h2 + l2)
-// is two 16x16x32 MFMAs whose K slots hold [h1 | l1] against [h2 | h2] and
-// [l2 | l2], leaving a relative error near 2^-16 in those terms.  Only the
-// 16x16x32 bf16 and 16x16x4 fp32 matrix instructions are used.  fp32 inputs run the same
-// schedule on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).
+// shows up in o or S (Sd, QE, T, X, U, P and Kd) are bf16 hi + lo pairs; a
+// pair-by-pair product (h1 + l1)(h2 + l2) is two 16x16x32 MFMAs whose K slots
+// hold [h1 | l1] against [h2 | h2] and [l2 | l2] (three for QE Sd, where the
+// K slots are all channels), leaving a relative error near 2^-16.  Only -KE
+// (in X and A) is a single bf16.  fp32 inputs run the same schedule on the
+// fp32 matrix cores (v_mfma_f32_16x16x4_f32).
 #include <type_traits>
 
 #include "kda_device.h"
@@ -75,23 +83,77 @@ __device__ __forceinline__ f32x4 from_bf4(bf16x4 x)
 {
     return f32x4{bf2f(x[0]), bf2f(x[1]), bf2f(x[2]), bf2f(x[3])};
 }
+__device__ __forceinline__ int64_t uniform64(int64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// value of x in lane `lane` (wave-uniform result)
+__device__ __forceinline__ float bcast(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// hi/lo split of a D-layout tile packed as 32-deep B operands [hi; hi], [lo; lo]
+__device__ __forceinline__ void split_hl(f32x4 x, bf16x8 &hh, bf16x8 &ll)
+{
+    const bf16x4 h = to_bf4(x);
+    const bf16x4 l = to_bf4(x - from_bf4(h));
+    hh = cat(h, h);
+    ll = cat(l, l);
+}
+
+// Raw buffer resources: an access at a byte offset >= num_records reads 0
+// and a store there is dropped, so per-chunk resources sized to the chunk's
+// real tokens mask the ragged tail without branches (and every load and
+// store of the main loop is issued unconditionally).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int n = bytes > 0 ? (int)bytes : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 bload64(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, int off, bf16 x)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, x), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, int off, float x)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // configuration
 // ---------------------------------------------------------------------------
-template <typename TI, int DK_, int NW_>
+template <typename TI, int DK_, int NW_, int NBUF_>
 struct Cfg {
     static constexpr bool BF = std::is_same<TI, bf16>::value;
     using OT = typename std::conditional<BF, bf16, float>::type;   // LDS operand type
     static constexpr int DK = DK_;
     static constexpr int NW = NW_;                 // consumer waves
+    static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
     static constexpr int NT = (NW + 1) * WAVE;     // + one helper wave
     static constexpr int NC = NW * WAVE;           // consumer threads
     static constexpr int LDK = DK + (BF ? 8 : 4);  // row stride of [16][DK] arrays
-    static constexpr int LDT = BF ? 24 : 20;       // row stride of [*][16] arrays
+    static constexpr int LDT = 20;                 // row stride of Kd^T [DK][16]
+    static constexpr int LDP = BF ? 24 : 20;       // row stride of T, P [16][16]
     static constexpr int LDV = BV + (BF ? 8 : 4);
-    static constexpr int LDO = BV + 4;
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
     static constexpr int CW = DK / NW;
     static constexpr int CPW = CW / 2;
@@ -100,49 +162,67 @@ struct Cfg {
     static constexpr int LO = BF ? 1 : 0;          // hi/lo split present
     static_assert(CW >= 16 && CW <= 128, "builder mapping needs 16 <= d_k/NW <= 128");
     static_assert(NG * TPG == 16, "token groups");
+    static_assert(NBUF == 2 || NBUF == 3, "operand ring depth");
 };
 
 template <class C>
-struct Buf {
+struct alignas(16) Buf {
     using OT = typename C::OT;
-    OT NL[16][C::LDK];                   // -Kt (single precision operand)
-    OT QH[16][C::LDK];                   // Qt hi
-    OT QL[C::LO ? 16 : 1][C::LDK];       // Qt lo
-    OT RH[16][C::LDK];                   // Kh hi
-    OT RL[C::LO ? 16 : 1][C::LDK];       // Kh lo
-    OT KH[C::DK][C::LDT];                // Kd^T hi   [channel][token]
+    OT NK[16][C::LDK];                   // -KE                  [token][channel]
+    OT QH[16][C::LDK];                   // QE hi
+    OT QL[C::LO ? 16 : 1][C::LDK];       // QE lo
+    OT DH[16][C::LDK];                   // Kd hi                [token][channel]
+    OT DL[C::LO ? 16 : 1][C::LDK];       // Kd lo
+    OT KH[C::DK][C::LDT];                // Kd^T hi              [channel][token]
     OT KL[C::LO ? C::DK : 1][C::LDT];    // Kd^T lo
-    OT TH[16][C::LDT];                   // T hi      [token r][token i]
-    OT TL[C::LO ? 16 : 1][C::LDT];
-    OT PH[16][C::LDT];                   // P hi
-    OT PL[C::LO ? 16 : 1][C::LDT];
+    OT TH[16][C::LDP];                   // T hi                 [token r][token i]
+    OT TL[C::LO ? 16 : 1][C::LDP];
+    OT PH[16][C::LDP];                   // P hi
+    OT PL[C::LO ? 16 : 1][C::LDP];
     OT V[16][C::LDV];                    // value block
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
 };
 
 template <class C>
-struct Smem {
-    Buf<C> buf[3];
-    float AF[16][17];                    // helper: A in fp32
-    float OB[2][16][C::LDO];             // output staging
+struct alignas(16) Smem {
+    Buf<C> buf[C::NBUF];
+    float AF[16][20];                    // helper: A in fp32, row-major
 };
 
-// raw (un-scaled) chunk inputs held in registers between load and build
+// raw (un-scaled) chunk inputs held in registers between load and build,
+// as the bits the buffer loads return (zero past the sequence end)
 template <class C>
 struct Raw {
-    using TI = typename std::conditional<C::BF, bf16, float>::type;
-    typedef TI TI2 __attribute__((ext_vector_type(2)));
-    TI2 q[C::TPG], k[C::TPG];
-    f32x2 g[C::TPG];
-    typedef TI TI4 __attribute__((ext_vector_type(4)));
-    TI4 v;
-    float beta;
+    typedef typename std::conditional<C::BF, uint32_t, u32x2>::type P2;   // 2 q/k elements
+    typedef typename std::conditional<C::BF, u32x2, u32x4>::type P4;      // 4 v elements
+    P2 q[C::TPG], k[C::TPG];
+    u32x2 g[C::TPG];
+    P4 v;
+    uint32_t beta;
 };
 
+template <class C>
+__device__ __forceinline__ float elem(typename Raw<C>::P2 x, int i)
+{
+    if constexpr (C::BF) return u16_to_f(i ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffffu));
+    else return __uint_as_float(x[i]);
+}
+template <class C>
+__device__ __forceinline__ float elem4(typename Raw<C>::P4 x, int i)
+{
+    if constexpr (C::BF) {
+        const uint32_t w = x[i >> 1];
+        return u16_to_f((i & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu));
+    } else {
+        return __uint_as_float(x[i]);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// loads of one chunk's raw inputs (masked past the sequence end: the padded
-// tokens have k = q = v = 0, g = 0, beta = 0, an exact identity transition)
+// loads of one chunk's raw inputs through buffer resources bounded by the
+// chunk's real tokens: padded tokens read k = q = v = 0, g = 0, beta = 0,
+// an exact identity transition.  ntok may be <= 0 (nothing is read).
 // ---------------------------------------------------------------------------
 template <class C, typename TI>
 __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
@@ -152,67 +232,54 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
                                          int ntok, int H, int h, int DV, int col_base,
                                          int wave, int lane, int tid)
 {
-    using R = Raw<C>;
+    constexpr int ES = sizeof(TI);
+    const int64_t rowk = (int64_t)H * C::DK, rowv = (int64_t)H * DV;
+    const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * ES);
+    const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * ES);
+    const rsrc_t rg = make_rsrc(g + tok_base * rowk, ntok * rowk * 4);
+    const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok * rowv * ES);
+    const rsrc_t rb = make_rsrc(beta + tok_base * H, (int64_t)ntok * H * 4);
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
 #pragma unroll
     for (int t = 0; t < C::TPG; ++t) {
-        const int tok = tg * C::TPG + t;
-        if (tok < ntok) {
-            const int64_t e = ((tok_base + tok) * H + h) * (int64_t)C::DK + ch;
-            r.q[t] = *reinterpret_cast<const typename R::TI2 *>(q + e);
-            r.k[t] = *reinterpret_cast<const typename R::TI2 *>(k + e);
-            r.g[t] = *reinterpret_cast<const f32x2 *>(g + e);
+        const int e = (tg * C::TPG + t) * (int)rowk + h * C::DK + ch;
+        if constexpr (C::BF) {
+            r.q[t] = bload32(rq, e * ES);
+            r.k[t] = bload32(rk, e * ES);
         } else {
-            r.q[t] = typename R::TI2{(TI)0.f, (TI)0.f};
-            r.k[t] = typename R::TI2{(TI)0.f, (TI)0.f};
-            r.g[t] = f32x2{0.f, 0.f};
+            r.q[t] = bload64(rq, e * ES);
+            r.k[t] = bload64(rk, e * ES);
         }
+        r.g[t] = bload64(rg, e * 4);
     }
-    {
-        const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-        if (row < ntok) {
-            const int64_t e = ((tok_base + row) * H + h) * (int64_t)DV + col_base + 4 * c4;
-            r.v = *reinterpret_cast<const typename R::TI4 *>(v + e);
-        } else {
-            r.v = typename R::TI4{(TI)0.f, (TI)0.f, (TI)0.f, (TI)0.f};
-        }
-    }
-    r.beta = (tid < ntok) ? beta[(tok_base + tid) * H + h] : 0.f;
+    const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
+    const int ev = row * (int)rowv + h * DV + col_base + 4 * c4;
+    if constexpr (C::BF) r.v = bload64(rv, ev * ES);
+    else r.v = bload128(rv, ev * ES);
+    r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
 }
 
 // ---------------------------------------------------------------------------
-// build: raw registers -> decay-scaled operands of one chunk in LDS
+// build: raw registers -> end-referenced operands of one chunk in LDS
 // ---------------------------------------------------------------------------
-template <class C>
-__device__ __forceinline__ void store_pair(typename C::OT *hi, typename C::OT *lo, float a, float b)
-{
-    using OT = typename C::OT;
-    typedef OT OT2 __attribute__((ext_vector_type(2)));
-    if constexpr (C::BF) {
-        const bf16 ah = f2bf(a), bh = f2bf(b);
-        *reinterpret_cast<OT2 *>(hi) = OT2{ah, bh};
-        *reinterpret_cast<OT2 *>(lo) = OT2{f2bf(a - bf2f(ah)), f2bf(b - bf2f(bh))};
-    } else {
-        *reinterpret_cast<OT2 *>(hi) = OT2{a, b};
-    }
-}
-
 template <class C>
 __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int lane, int tid)
 {
     using OT = typename C::OT;
     typedef OT OT2 __attribute__((ext_vector_type(2)));
+    constexpr int TPG = C::TPG;
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
+    const int tok0 = tg * TPG;
 
     // cumulative log2-decay over this lane's tokens, then across token groups
-    float G0[C::TPG], G1[C::TPG];
+    float G0[TPG], G1[TPG];
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int t = 0; t < C::TPG; ++t) {
-        s0 += r.g[t][0] * LOG2E;
-        s1 += r.g[t][1] * LOG2E;
+    for (int t = 0; t < TPG; ++t) {
+        s0 = __builtin_fmaf(__uint_as_float(r.g[t][0]), LOG2E, s0);
+        s1 = __builtin_fmaf(__uint_as_float(r.g[t][1]), LOG2E, s1);
         G0[t] = s0;
         G1[t] = s1;
     }
@@ -223,33 +290,62 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         const float n1 = __shfl_up(i1, off * C::CPW, WAVE);
         if (tg >= off) { i0 += n0; i1 += n1; }
     }
-    const float e0 = i0 - s0, e1 = i1 - s1;                  // exclusive offsets
     const int last = cp + (C::NG - 1) * C::CPW;
     const float T0 = __shfl(i0, last, WAVE), T1 = __shfl(i1, last, WAVE);  // Gc_16
-    const float inv0 = fast_exp2(-T0), inv1 = fast_exp2(-T1);
+    // Gc_r - Gc_16 = (local prefix + exclusive offset) - total
+    const float o0 = i0 - s0 - T0, o1 = i1 - s1 - T1;
 
+    OT kdh0[TPG], kdh1[TPG], kdl0[TPG], kdl1[TPG];
 #pragma unroll
-    for (int t = 0; t < C::TPG; ++t) {
-        const int tok = tg * C::TPG + t;
-        const float ga = G0[t] + e0, gb = G1[t] + e1;
-        const float pa = fast_exp2(ga), pb = fast_exp2(gb);           // e^{Gc}
-        const float sa = fast_exp2(T0 - ga), sb = fast_exp2(T1 - gb); // e^{Gc_16 - Gc}
-        const float ka = (float)r.k[t][0], kb = (float)r.k[t][1];
-        const float qa = (float)r.q[t][0], qb = (float)r.q[t][1];
-        *reinterpret_cast<OT2 *>(&B.NL[tok][ch]) = OT2{(OT)(-ka * pa), (OT)(-kb * pb)};
-        store_pair<C>(&B.QH[tok][ch], &B.QL[C::LO ? tok : 0][ch], qa * pa, qb * pb);
-        const float da = ka * sa, db = kb * sb;                       // Kd
-        store_pair<C>(&B.RH[tok][ch], &B.RL[C::LO ? tok : 0][ch], da * inv0, db * inv1);
-        // Kd^T: [channel][token]
+    for (int t = 0; t < TPG; ++t) {
+        const int tok = tok0 + t;
+        const float d0 = G0[t] + o0, d1 = G1[t] + o1;                 // >= 0 (log2)
+        const float e0 = fast_exp2(d0), e1 = fast_exp2(d1);           // E
+        const float f0 = fast_exp2(-d0), f1 = fast_exp2(-d1);         // 1 / E
+        const float ka = elem<C>(r.k[t], 0), kb = elem<C>(r.k[t], 1);
+        const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
+        *reinterpret_cast<OT2 *>(&B.NK[tok][ch]) = OT2{(OT)(-ka * e0), (OT)(-kb * e1)};
+        const float qe0 = qa * e0, qe1 = qb * e1;
+        const float kd0 = ka * f0, kd1 = kb * f1;
         if constexpr (C::BF) {
-            const bf16 ha = f2bf(da), hb = f2bf(db);
-            B.KH[ch][tok] = ha;
-            B.KH[ch + 1][tok] = hb;
-            B.KL[ch][tok] = f2bf(da - bf2f(ha));
-            B.KL[ch + 1][tok] = f2bf(db - bf2f(hb));
+            const bf16 qh0 = f2bf(qe0), qh1 = f2bf(qe1);
+            const bf16 dh0 = f2bf(kd0), dh1 = f2bf(kd1);
+            const bf16 dl0 = f2bf(kd0 - bf2f(dh0)), dl1 = f2bf(kd1 - bf2f(dh1));
+            *reinterpret_cast<OT2 *>(&B.QH[tok][ch]) = OT2{qh0, qh1};
+            *reinterpret_cast<OT2 *>(&B.QL[tok][ch]) =
+                OT2{f2bf(qe0 - bf2f(qh0)), f2bf(qe1 - bf2f(qh1))};
+            *reinterpret_cast<OT2 *>(&B.DH[tok][ch]) = OT2{dh0, dh1};
+            *reinterpret_cast<OT2 *>(&B.DL[tok][ch]) = OT2{dl0, dl1};
+            kdh0[t] = dh0; kdh1[t] = dh1; kdl0[t] = dl0; kdl1[t] = dl1;
         } else {
-            B.KH[ch][tok] = da;
-            B.KH[ch + 1][tok] = db;
+            *reinterpret_cast<OT2 *>(&B.QH[tok][ch]) = OT2{qe0, qe1};
+            *reinterpret_cast<OT2 *>(&B.DH[tok][ch]) = OT2{kd0, kd1};
+            kdh0[t] = kd0; kdh1[t] = kd1;
+        }
+    }
+    // Kd^T rows: this lane's TPG consecutive tokens of channels ch, ch + 1,
+    // written as vectors of (up to) four
+    if constexpr (TPG == 2) {
+        *reinterpret_cast<OT2 *>(&B.KH[ch][tok0]) = OT2{kdh0[0], kdh0[1]};
+        *reinterpret_cast<OT2 *>(&B.KH[ch + 1][tok0]) = OT2{kdh1[0], kdh1[1]};
+        if constexpr (C::BF) {
+            *reinterpret_cast<OT2 *>(&B.KL[ch][tok0]) = OT2{kdl0[0], kdl0[1]};
+            *reinterpret_cast<OT2 *>(&B.KL[ch + 1][tok0]) = OT2{kdl1[0], kdl1[1]};
+        }
+    } else {
+        typedef OT OT4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int t = 0; t < TPG; t += 4) {
+            *reinterpret_cast<OT4 *>(&B.KH[ch][tok0 + t]) =
+                OT4{kdh0[t], kdh0[t + 1], kdh0[t + 2], kdh0[t + 3]};
+            *reinterpret_cast<OT4 *>(&B.KH[ch + 1][tok0 + t]) =
+                OT4{kdh1[t], kdh1[t + 1], kdh1[t + 2], kdh1[t + 3]};
+            if constexpr (C::BF) {
+                *reinterpret_cast<OT4 *>(&B.KL[ch][tok0 + t]) =
+                    OT4{kdl0[t], kdl0[t + 1], kdl0[t + 2], kdl0[t + 3]};
+                *reinterpret_cast<OT4 *>(&B.KL[ch + 1][tok0 + t]) =
+                    OT4{kdl1[t], kdl1[t + 1], kdl1[t + 2], kdl1[t + 3]};
+            }
         }
     }
     if (tg == 0) {
@@ -260,176 +356,205 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
         typedef OT OT4 __attribute__((ext_vector_type(4)));
         *reinterpret_cast<OT4 *>(&B.V[row][4 * c4]) =
-            OT4{(OT)(float)r.v[0], (OT)(float)r.v[1], (OT)(float)r.v[2], (OT)(float)r.v[3]};
+            OT4{(OT)elem4<C>(r.v, 0), (OT)elem4<C>(r.v, 1), (OT)elem4<C>(r.v, 2),
+                (OT)elem4<C>(r.v, 3)};
     }
-    if (tid < 16) B.BETA[tid] = r.beta;
+    if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
 }
 
 // ---------------------------------------------------------------------------
 // helper wave: A, P and T = (I + A)^{-1} Diag(beta) for one chunk
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[17], int lane)
+__device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
 {
+    using OT = typename C::OT;
     const int j = lane & 15, g4 = lane >> 4;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // at[e] (lane (j, g4)) = -(KE_j . Kd_{4 g4 + e})           (A before beta)
+    // pt[e] (lane (j, g4)) =   QE_j . Kd_{4 g4 + e} = P[j][4 g4 + e]
+    // Operands are ordered so that each lane ends up holding a row segment
+    // (row j, columns 4 g4 .. 4 g4 + 3), which it writes as one vector.
+    f32x4 at = zero, pt = zero;
     if constexpr (C::BF) {
+        f32x4 p2 = zero, p3 = zero;               // three independent chains
         if constexpr (C::DK >= 32) {
             // K slot (g4, i) = channel 32 s + 8 g4 + i on both operands
 #pragma unroll
             for (int s = 0; s < C::DK / 32; ++s) {
                 const int kk = 32 * s + 8 * g4;
-                const bf16x8 nl = ld8b(&B.NL[j][kk]);
+                const bf16x8 nk = ld8b(&B.NK[j][kk]);
                 const bf16x8 qh = ld8b(&B.QH[j][kk]), ql = ld8b(&B.QL[j][kk]);
-                const bf16x8 rh = ld8b(&B.RH[j][kk]), rl = ld8b(&B.RL[j][kk]);
-                a = mma32(nl, rh, a);
-                p = mma32(qh, rh, p);
-                p = mma32(qh, rl, p);
-                p = mma32(ql, rh, p);
+                const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
+                at = mma32(dh, nk, at);
+                pt = mma32(dh, qh, pt);
+                p2 = mma32(dl, qh, p2);
+                p3 = mma32(dh, ql, p3);
             }
         } else {
             // d_k = 16: K slot (g4, i) = channel 4 g4 + i%4 of the hi (i < 4)
             // or lo (i >= 4) part
             const int kk = 4 * g4;
-            const bf16x4 nl = ld4b(&B.NL[j][kk]);
+            const bf16x4 nk = ld4b(&B.NK[j][kk]);
             const bf16x4 qh = ld4b(&B.QH[j][kk]), ql = ld4b(&B.QL[j][kk]);
-            const bf16x4 rh = ld4b(&B.RH[j][kk]), rl = ld4b(&B.RL[j][kk]);
+            const bf16x4 dh = ld4b(&B.DH[j][kk]);
+            const bf16x8 dd = cat(dh, ld4b(&B.DL[j][kk]));
             const bf16x4 z = {};
-            a = mma32(cat(nl, z), cat(rh, z), a);
-            p = mma32(cat(qh, ql), cat(rh, rh), p);      // (qh + ql) rh
-            p = mma32(cat(qh, ql), cat(rl, rl), p);      // (qh + ql) rl
+            at = mma32(cat(dh, z), cat(nk, z), at);
+            pt = mma32(dd, cat(qh, qh), pt);    // (dh + dl) qh
+            p2 = mma32(dd, cat(ql, ql), p2);    // (dh + dl) ql
         }
+        pt += p2 + p3;
     } else {
 #pragma unroll 8
         for (int s = 0; s < C::DK / 4; ++s) {
             const int kk = 4 * s + g4;
-            a = mma4(B.NL[j][kk], B.RH[j][kk], a);
-            p = mma4(B.QH[j][kk], B.RH[j][kk], p);
+            at = mma4(B.DH[j][kk], B.NK[j][kk], at);
+            pt = mma4(B.DH[j][kk], B.QH[j][kk], pt);
         }
     }
-    // D layout: element i of lane (j, g4) is row r = 4 g4 + i, column j.
-    // A_{ri} = beta_r Kt_r . Kh_i for i < r; NL = -Kt, hence the sign.
+    typedef OT OT4 __attribute__((ext_vector_type(4)));
+    {
+        // P row j (lower triangle including the diagonal)
+        float pv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g4 + i;
-        AF[r][j] = (j < r) ? -B.BETA[r] * a[i] : 0.f;
-        const float pv = (j <= r) ? p[i] : 0.f;
+        for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e <= j) ? pt[e] : 0.f;
         if constexpr (C::BF) {
-            const bf16 ph = f2bf(pv);
-            B.PH[r][j] = ph;
-            B.PL[r][j] = f2bf(pv - bf2f(ph));
+            const bf16x4 h = {f2bf(pv[0]), f2bf(pv[1]), f2bf(pv[2]), f2bf(pv[3])};
+            *reinterpret_cast<bf16x4 *>(&B.PH[j][4 * g4]) = h;
+            *reinterpret_cast<bf16x4 *>(&B.PL[j][4 * g4]) =
+                bf16x4{f2bf(pv[0] - bf2f(h[0])), f2bf(pv[1] - bf2f(h[1])),
+                       f2bf(pv[2] - bf2f(h[2])), f2bf(pv[3] - bf2f(h[3]))};
         } else {
-            B.PH[r][j] = pv;
+            *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
+        // A row j: A_{jc} = beta_j KE_j . Kd_c for c < j (NK = -KE)
+        const float bj = B.BETA[j];
+        f32x4 av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = (4 * g4 + e < j) ? -bj * at[e] : 0.f;
+        *reinterpret_cast<f32x4 *>(&AF[j][4 * g4]) = av;
     }
     // make this wave's AF writes visible to its own later reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < 16) {
-        // column j of (I + A)^{-1}: forward substitution, fp32
-        float t[16];
+    // Row j of T' = (I + A)^{-1} from T' (I + A) = I, right-looking: once
+    // T'_{j,i} is final (i from 15 down), it is removed from every column
+    // c < i.  The critical path is one FMA per column; row i of A is read
+    // from LDS as a broadcast (every lane reads the same address).  Every
+    // lane runs row lane % 16; lanes 0..15 write it.
+    float acc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == j) ? 1.f : 0.f;
+    for (int c = 0; c < 16; ++c) acc[c] = (c == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) acc -= AF[r][i] * t[i];
-            t[r] = acc;
+    for (int i = 15; i >= 1; --i) {
+        const float ti = acc[i];
+#pragma unroll
+        for (int c4 = 0; c4 < i; c4 += 4) {
+            const f32x4 ar = *reinterpret_cast<const f32x4 *>(&AF[i][c4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c4 + e < i) acc[c4 + e] = __builtin_fmaf(-ar[e], ti, acc[c4 + e]);
         }
-        const float bj = B.BETA[j];
+    }
+    if (lane < 16) {
+        // T = T' Diag(beta): column c scaled by beta_c
+        float tv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float tv = t[r] * bj;
+        for (int c4 = 0; c4 < 16; c4 += 4) {
+            const f32x4 bb = *reinterpret_cast<const f32x4 *>(&B.BETA[c4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tv[c4 + e] = acc[c4 + e] * bb[e];
+        }
+#pragma unroll
+        for (int c0 = 0; c0 < 16; c0 += 4) {
             if constexpr (C::BF) {
-                const bf16 th = f2bf(tv);
-                B.TH[r][j] = th;
-                B.TL[r][j] = f2bf(tv - bf2f(th));
+                const bf16x4 h = {f2bf(tv[c0]), f2bf(tv[c0 + 1]), f2bf(tv[c0 + 2]),
+                                  f2bf(tv[c0 + 3])};
+                *reinterpret_cast<bf16x4 *>(&B.TH[j][c0]) = h;
+                *reinterpret_cast<bf16x4 *>(&B.TL[j][c0]) =
+                    bf16x4{f2bf(tv[c0] - bf2f(h[0])), f2bf(tv[c0 + 1] - bf2f(h[1])),
+                           f2bf(tv[c0 + 2] - bf2f(h[2])), f2bf(tv[c0 + 3] - bf2f(h[3]))};
             } else {
-                B.TH[r][j] = tv;
+                *reinterpret_cast<OT4 *>(&B.TH[j][c0]) =
+                    OT4{tv[c0], tv[c0 + 1], tv[c0 + 2], tv[c0 + 3]};
             }
         }
     }
 }
 
-// hi/lo bf16 split of a D-layout tile, packed as 32-deep B operands:
-// hh = [hi; hi], ll = [lo; lo] (slot (g4, i) = row 4 g4 + i%4)
-__device__ __forceinline__ void split_hl(f32x4 x, bf16x8 &hh, bf16x8 &ll)
-{
-    const bf16x4 h = to_bf4(x);
-    const bf16x4 l = to_bf4(x - from_bf4(h));
-    hh = cat(h, h);
-    ll = cat(l, l);
-}
-
 // ---------------------------------------------------------------------------
-// consumer wave: the S-dependent chain of one chunk
+// consumer wave: the S-dependent chain of one chunk; returns O (D layout)
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16],
-                                        float (*OB)[C::LDO], int wave, int lane)
+__device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16], int wave,
+                                         int lane)
 {
     const int j = lane & 15, g4 = lane >> 4;
     const int vc = 16 * wave + j;           // column inside the block
-    f32x4 x, u, o = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 x, u, o = zero, x2 = zero, o2 = zero, o3 = zero;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)B.V[4 * g4 + i][vc];
+    // Sd = Diag(e^{Gc_16}) S
+#pragma unroll
+    for (int t = 0; t < C::DK / 16; ++t)
+        S[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 
     if constexpr (C::BF) {
-        // S as a bf16 hi/lo pair of B operands.  For d_k >= 32 the K slot
+        // Sd as a bf16 hi/lo pair of B operands.  For d_k >= 32 the K slot
         // (g4, i) of step s is channel 32 s + 4 g4 + i (i < 4, tile 2s) or
         // 32 s + 16 + 4 g4 + (i - 4) (tile 2s + 1); A operands are read with
         // the same assignment, so each product is an exact contraction.
         if constexpr (C::DK >= 32) {
             constexpr int NS = C::DK / 32;
-            bf16x8 sh[NS], sl[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const bf16x4 h0 = to_bf4(S[2 * s]), h1 = to_bf4(S[2 * s + 1]);
-                sh[s] = cat(h0, h1);
-                sl[s] = cat(to_bf4(S[2 * s] - from_bf4(h0)), to_bf4(S[2 * s + 1] - from_bf4(h1)));
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
+                const bf16x8 sh = cat(h0, h1);
+                const bf16x8 sl = cat(to_bf4(S[2 * s] - from_bf4(h0)),
+                                      to_bf4(S[2 * s + 1] - from_bf4(h1)));
                 const int kk = 32 * s + 4 * g4;
-                const bf16x8 nl = cat(ld4b(&B.NL[j][kk]), ld4b(&B.NL[j][kk + 16]));
+                const bf16x8 nk = cat(ld4b(&B.NK[j][kk]), ld4b(&B.NK[j][kk + 16]));
                 const bf16x8 qh = cat(ld4b(&B.QH[j][kk]), ld4b(&B.QH[j][kk + 16]));
                 const bf16x8 ql = cat(ld4b(&B.QL[j][kk]), ld4b(&B.QL[j][kk + 16]));
-                x = mma32(nl, sh[s], x);
-                x = mma32(nl, sl[s], x);
-                o = mma32(qh, sh[s], o);            // Qt S: the lo x lo term
-                o = mma32(qh, sl[s], o);            // (2^-18) is dropped
-                o = mma32(ql, sh[s], o);
+                x = mma32(nk, sh, x);
+                x2 = mma32(nk, sl, x2);
+                o = mma32(qh, sh, o);            // QE Sd: the lo x lo term
+                o2 = mma32(qh, sl, o2);          // (2^-18) is dropped
+                o3 = mma32(ql, sh, o3);
             }
+            x += x2;
+            o += o2 + o3;
         } else {
-            // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of S hi (i < 4) or lo
-            const bf16x4 h = to_bf4(S[0]);
-            const bf16x8 shl = cat(h, to_bf4(S[0] - from_bf4(h)));
-            const bf16x4 nl = ld4b(&B.NL[j][4 * g4]);
+            // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
+            const bf16x4 hh = to_bf4(S[0]);
+            const bf16x4 ll = to_bf4(S[0] - from_bf4(hh));
+            const bf16x4 nk = ld4b(&B.NK[j][4 * g4]);
             const bf16x8 qq = cat(ld4b(&B.QH[j][4 * g4]), ld4b(&B.QL[j][4 * g4]));
-            x = mma32(cat(nl, nl), shl, x);
-            o = mma32(qq, cat(h, h), o);                     // (Qh + Ql) Sh
-            o = mma32(qq, cat(shl.hi, shl.hi), o);           // (Qh + Ql) Sl
+            x = mma32(cat(nk, nk), cat(hh, ll), x);
+            o = mma32(qq, cat(hh, hh), o);                   // (Qh + Ql) Sh
+            o = mma32(qq, cat(ll, ll), o);                   // (Qh + Ql) Sl
         }
         // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
         bf16x8 xhh, xll, uhh, ull;
         split_hl(x, xhh, xll);
-        const bf16x8 t = cat(ld4b(&B.TH[j][4 * g4]), ld4b(&B.TL[j][4 * g4]));
-        u = mma32(t, xhh, f32x4{0.f, 0.f, 0.f, 0.f});
-        u = mma32(t, xll, u);
+        const bf16x8 tt = cat(ld4b(&B.TH[j][4 * g4]), ld4b(&B.TL[j][4 * g4]));
+        u = mma32(tt, xhh, zero);
+        u = mma32(tt, xll, u);
         split_hl(u, uhh, ull);
         // O += P U
         const bf16x8 pp = cat(ld4b(&B.PH[j][4 * g4]), ld4b(&B.PL[j][4 * g4]));
         o = mma32(pp, uhh, o);
         o = mma32(pp, ull, o);
-        // S <- Diag(e^{Gc_16}) S + Kd^T U
+        // S' = Sd + Kd^T U
 #pragma unroll
-        for (int t4 = 0; t4 < C::DK / 16; ++t4) {
-            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t4 + 4 * g4]);
-            const bf16x8 kd = cat(ld4b(&B.KH[16 * t4 + j][4 * g4]),
-                                  ld4b(&B.KL[16 * t4 + j][4 * g4]));
-            S[t4] *= dec;
-            S[t4] = mma32(kd, uhh, S[t4]);
-            S[t4] = mma32(kd, ull, S[t4]);
+        for (int t = 0; t < C::DK / 16; ++t) {
+            const bf16x8 kd = cat(ld4b(&B.KH[16 * t + j][4 * g4]),
+                                  ld4b(&B.KL[16 * t + j][4 * g4]));
+            S[t] = mma32(kd, uhh, S[t]);
+            S[t] = mma32(kd, ull, S[t]);
         }
     } else {
         // fp32: K index of slot (g4) in step (t, i) is 16 t + 4 g4 + i
@@ -438,7 +563,7 @@ __device__ __forceinline__ void consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16],
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int kk = 16 * t + 4 * g4 + i;
-                x = mma4(B.NL[j][kk], S[t][i], x);
+                x = mma4(B.NK[j][kk], S[t][i], x);
                 o = mma4(B.QH[j][kk], S[t][i], o);
             }
         }
@@ -449,21 +574,18 @@ __device__ __forceinline__ void consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16],
         for (int i = 0; i < 4; ++i) o = mma4(B.PH[j][4 * g4 + i], u[i], o);
 #pragma unroll
         for (int t = 0; t < C::DK / 16; ++t) {
-            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
-            S[t] *= dec;
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[t] = mma4(B.KH[16 * t + j][4 * g4 + i], u[i], S[t]);
         }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) OB[4 * g4 + i][vc] = o[i];
+    return o;
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int DK, int DV, int NW>
-__global__ __launch_bounds__((Cfg<TI, DK, NW>::NT))
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
+__global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF>::NT), (NBUF == 2 ? 3 : 1))
 void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                         const TI *__restrict__ v, const float *__restrict__ g,
                         const float *__restrict__ beta, const float *__restrict__ S0,
@@ -471,8 +593,9 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                         int32_t n_chains, int32_t H, TO *__restrict__ o,
                         float *__restrict__ S_T)
 {
-    using C = Cfg<TI, DK, NW>;
+    using C = Cfg<TI, DK, NW, NBUF>;
     constexpr int NB = DV / C::BV;
+    constexpr int LAG = NBUF - 1;            // build runs LAG chunks ahead
     __shared__ Smem<C> sm;
 
     // workgroup -> (chain, column block); the NB blocks of a chain share an
@@ -493,10 +616,16 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         bos = (int64_t)n * seqlen;
         T = seqlen;
     }
+    // wave-uniform values are made visibly uniform (readfirstlane) so that
+    // branches on them are scalar and the buffer resources built from them
+    // live in scalar registers
+    bos = uniform64(bos);
+    T = uniform64(T);
     const int nch = (int)((T + 15) / 16);
     const int col_base = vb * C::BV;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool is_helper = wave == NW;
     const int j = lane & 15, g4 = lane >> 4;
 
@@ -511,78 +640,84 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                 S[t][i] = S0 ? S0[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] : 0.f;
     }
 
+    // Prologue: build the first LAG chunks (and form A, P, T of chunk 0).
+    // Main loop, chunk c: build chunk c + LAG, load chunk c + LAG + 1,
+    // consume chunk c, form A, P, T of chunk c + 1.  Every global load and
+    // store of the main loop is issued unconditionally (buffer resources of
+    // chunks past the end are empty), so the compiler's memory-counter waits
+    // before a build cover exactly the loads that build needs.
     Raw<C> raw;
-    if (!is_helper && nch > 0)
-        load_raw<C>(raw, q, k, v, g, beta, bos, (int)(T < 16 ? T : 16), H, h, DV, col_base,
-                    wave, lane, tid);
-
-    for (int c = -2; c < nch; ++c) {
+    auto ntok_of = [&](int cc) -> int {
+        const int64_t rem = T - 16 * (int64_t)cc;
+        return (int)(rem < 0 ? 0 : (rem < 16 ? rem : 16));
+    };
+    if (!is_helper)
+        load_raw<C>(raw, q, k, v, g, beta, bos, ntok_of(0), H, h, DV, col_base, wave, lane, tid);
+#pragma unroll 1
+    for (int c = -LAG; c < 0; ++c) {
         if (!is_helper) {
-            const int cb = c + 2;             // chunk to build
-            if (cb < nch) {
-                build<C>(sm.buf[cb % 3], raw, wave, lane, tid);
-                const int cl = c + 3;         // chunk to load
-                if (cl < nch) {
-                    const int64_t rem = T - 16 * (int64_t)cl;
-                    load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cl,
-                                (int)(rem < 16 ? rem : 16), H, h, DV, col_base, wave, lane, tid);
-                }
-            }
-            if (c >= 1) {                     // write out chunk c - 1
-                const int cs = c - 1;
-                const int64_t rem = T - 16 * (int64_t)cs;
-                const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-                if (row < rem) {
-                    const float *src = &sm.OB[cs & 1][row][4 * c4];
-                    const int64_t e = ((bos + 16 * (int64_t)cs + row) * H + h) * (int64_t)DV +
-                                      col_base + 4 * c4;
-                    Elem<TO>::st4(o + e, f32x4{src[0], src[1], src[2], src[3]});
-                }
-            }
-            if (c >= 0) consume<C>(sm.buf[c % 3], S, sm.OB[c & 1], wave, lane);
+            if (c + LAG < nch) build<C>(sm.buf[c + LAG], raw, wave, lane, tid);
+            const int cl = c + LAG + 1;
+            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cl, ntok_of(cl), H, h, DV,
+                        col_base, wave, lane, tid);
+        }
+        if constexpr (NBUF == 2) __syncthreads();
+        if (is_helper && c + 1 == 0 && nch > 0) helper<C>(sm.buf[0], sm.AF, lane);
+        __syncthreads();
+    }
+    // O of chunk c is written at the start of iteration c + 1, before that
+    // iteration's loads: the stores are then older than the loads the next
+    // build waits for, so that wait never includes store acknowledgements.
+    const int64_t rowo = (int64_t)H * DV;
+    const int ooff = (int)(h * DV + col_base + 16 * wave + j);
+    f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+    auto store_o = [&](int cc) {
+        const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
+                                    (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int64_t)sizeof(TO));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bstore(ro, (int)(((4 * g4 + i) * rowo + ooff) * sizeof(TO)), (TO)ov[i]);
+    };
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+        if (!is_helper) {
+            const int cb = c + LAG;
+            if (cb < nch) build<C>(sm.buf[cb % NBUF], raw, wave, lane, tid);
+            store_o(c - 1);
+            const int cl = cb + 1;
+            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cl, ntok_of(cl), H, h, DV,
+                        col_base, wave, lane, tid);
+        }
+        if constexpr (NBUF == 2) __syncthreads();
+        if (!is_helper) {
+            ov = consume<C>(sm.buf[c % NBUF], S, wave, lane);
         } else {
-            const int ch = c + 1;
-            if (ch >= 0 && ch < nch) helper<C>(sm.buf[ch % 3], sm.AF, lane);
+            if (c + 1 < nch) helper<C>(sm.buf[(c + 1) % NBUF], sm.AF, lane);
         }
         __syncthreads();
     }
-    if (!is_helper) {
-        if (nch >= 1) {
-            const int cs = nch - 1;
-            const int64_t rem = T - 16 * (int64_t)cs;
-            const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-            if (row < rem) {
-                const float *src = &sm.OB[cs & 1][row][4 * c4];
-                const int64_t e = ((bos + 16 * (int64_t)cs + row) * H + h) * (int64_t)DV +
-                                  col_base + 4 * c4;
-                Elem<TO>::st4(o + e, f32x4{src[0], src[1], src[2], src[3]});
-            }
-        }
-        if (S_T) {
+    if (!is_helper && nch > 0) store_o(nch - 1);
+    if (!is_helper && S_T) {
 #pragma unroll
-            for (int t = 0; t < DK / 16; ++t)
+        for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S_T[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
-        }
+            for (int i = 0; i < 4; ++i)
+                S_T[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
     }
 }
 
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int DK, int DV, int NW>
-static hipError_t launch_t(const PrefillArgs &a)
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
+static hipError_t launch_t(const PrefillArgs &a, int64_t chains)
 {
-    using C = Cfg<TI, DK, NW>;
+    using C = Cfg<TI, DK, NW, NBUF>;
     static_assert(DV % C::BV == 0, "column blocks");
     constexpr int NB = DV / C::BV;
-    const int64_t chains = (int64_t)a.n_seqs * a.H;
-    if (chains == 0) return hipSuccess;
-    if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
     const int64_t grid = ((chains + 7) / 8) * 8 * NB;
     if (grid * C::NT >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // grid size limit
-    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF>), dim3((unsigned)grid),
                        dim3(C::NT), 0, (hipStream_t)a.stream, (const TI *)a.q,
                        (const TI *)a.k, (const TI *)a.v, a.g, a.beta, a.S0, a.cu_seqlens,
                        a.seqlen, (int32_t)chains, a.H, (TO *)a.o, a.S_T);
@@ -597,11 +732,29 @@ struct PickNW {
     static constexpr int value = byv < bydk ? byv : bydk;
 };
 
+// Ring depth: with more workgroups than CUs, the two-deep ring (small enough
+// for two workgroups per CU) lets one workgroup run while the other waits at
+// a barrier; otherwise the three-deep ring needs one barrier per chunk.
+constexpr int64_t kNumCUs = 256;
+
+template <typename TI, typename TO, int DK, int DV>
+static hipError_t launch_dims(const PrefillArgs &a)
+{
+    constexpr int NW = PickNW<DK, DV>::value;
+    constexpr int NB = DV / (16 * NW);
+    const int64_t chains = (int64_t)a.n_seqs * a.H;
+    if (chains == 0) return hipSuccess;
+    if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
+    constexpr bool two_fit = sizeof(Smem<Cfg<TI, DK, NW, 2>>) <= 80 * 1024;
+    if (two_fit && chains * NB > kNumCUs) return launch_t<TI, TO, DK, DV, NW, 2>(a, chains);
+    return launch_t<TI, TO, DK, DV, NW, 3>(a, chains);
+}
+
 template <typename TI, typename TO>
 static hipError_t dispatch_dims(const PrefillArgs &a)
 {
 #define KDA_PF_CASE(DK_, DV_) \
-    if (a.d_k == DK_ && a.d_v == DV_) return launch_t<TI, TO, DK_, DV_, PickNW<DK_, DV_>::value>(a);
+    if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_>(a);
     KDA_PF_CASE(16, 16) KDA_PF_CASE(16, 32) KDA_PF_CASE(16, 64) KDA_PF_CASE(16, 128)
     KDA_PF_CASE(32, 16) KDA_PF_CASE(32, 32) KDA_PF_CASE(32, 64) KDA_PF_CASE(32, 128)
     KDA_PF_CASE(64, 16) KDA_PF_CASE(64, 32) KDA_PF_CASE(64, 64) KDA_PF_CASE(64, 128)
