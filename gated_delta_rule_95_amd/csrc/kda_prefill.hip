@@ -30,18 +30,16 @@
 //
 // Mapping.  One workgroup per (sequence, head, block of BV = 16 NW columns
 // of the state): the columns of S evolve independently, so the d_v split
-// needs no communication.  NW consumer waves and one helper wave:
+// needs no communication.  Three roles, 2 NW + 1 waves:
 //  * consumer wave w keeps S[:, 16w : 16w+16] of its block in registers in
 //    the 16x16 MFMA accumulator layout (lane l holds rows 4(l/16)+i, column
 //    l%16 of each 16x16 tile) and runs the S-dependent chain of chunk c;
-//  * the consumer waves together build the operands of chunk c+NBUF-1
-//    (cumulative sums, exponentials, bf16 hi/lo splits) into LDS from
-//    registers loaded one chunk earlier;
-//  * the helper wave forms A and P of chunk c+1 on the matrix cores and
-//    inverts (I + A) by forward substitution in fp32.
-// NBUF = 3: one barrier per chunk (build c+2 | helper c+1 | consume c).
-// NBUF = 2: two barriers per chunk, a smaller LDS footprint (two workgroups
-// fit on one CU).
+//  * builder wave w loads the raw inputs of a quarter of the key channels
+//    and builds the operands of chunk c+2 (cumulative sums, exponentials,
+//    bf16 hi/lo splits) into LDS;
+//  * the helper wave forms A and P of chunk c+1 and the inverse of (I + A)
+//    as a product of four factors, all on the matrix cores.
+// A ring of three LDS operand slots needs one barrier per chunk.
 //
 // Precision.  bf16 inputs: matrix-core operands are bf16 with fp32
 // accumulation; the state stays fp32 in registers.  Operands whose rounding
@@ -148,8 +146,8 @@ struct Cfg {
     static constexpr int NW = NW_;                 // consumer waves
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
-    static constexpr int NT = (NW + 1) * WAVE;     // + one helper wave
-    static constexpr int NC = NW * WAVE;           // consumer threads
+    static constexpr int NT = (2 * NW + 1) * WAVE; // consumers, builders, helper
+    static constexpr int NC = NW * WAVE;           // consumer (= builder) threads
     static constexpr int LDK = DK + (BF ? 8 : 4);  // row stride of [16][DK] arrays
     static constexpr int LDT = 20;                 // row stride of Kd^T [DK][16]
     static constexpr int LDP = BF ? 24 : 20;       // row stride of T, P [16][16]
@@ -162,7 +160,7 @@ struct Cfg {
     static constexpr int LO = BF ? 1 : 0;          // hi/lo split present
     static_assert(CW >= 16 && CW <= 128, "builder mapping needs 16 <= d_k/NW <= 128");
     static_assert(NG * TPG == 16, "token groups");
-    static_assert(NBUF == 2 || NBUF == 3, "operand ring depth");
+    static_assert(NBUF >= 3, "one barrier per chunk needs three ring slots");
 };
 
 template <class C>
@@ -187,7 +185,6 @@ struct alignas(16) Buf {
 template <class C>
 struct alignas(16) Smem {
     Buf<C> buf[C::NBUF];
-    float AF[16][20];                    // helper: A in fp32, row-major
 };
 
 // raw (un-scaled) chunk inputs held in registers between load and build,
@@ -363,21 +360,71 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
 }
 
 // ---------------------------------------------------------------------------
+// 16x16 products on the matrix cores between tiles held in the accumulator
+// (D) layout: lane (n, g) = (lane % 16, lane / 16) holds X[4 g + i][n].
+// A tile in D layout is directly a B operand when its K index 4 g + i sits in
+// the slots of group g; the left factor Y must then be given as Y^T in D
+// layout (lane (r, g) holds Y[r][4 g + i]).  So prod(YT, X) = Y X and
+// prod(X, YT) = X^T Y^T take the same two tiles with the roles swapped.
+// bf16: the tiles are hi/lo pairs and the product keeps all four terms,
+// [Yh | Yh] x [Xh ; Xl] + [Yl | Yl] x [Xh ; Xl].  fp32: four K=4 steps.
+// ---------------------------------------------------------------------------
+template <bool BF> struct Tile;
+template <> struct Tile<true> {
+    bf16x4 h, l;
+};
+template <> struct Tile<false> {
+    f32x4 x;
+};
+template <bool BF>
+__device__ __forceinline__ Tile<BF> to_tile(f32x4 x)
+{
+    if constexpr (BF) {
+        const bf16x4 h = to_bf4(x);
+        return Tile<true>{h, to_bf4(x - from_bf4(h))};
+    } else {
+        return Tile<false>{x};
+    }
+}
+template <bool BF>
+__device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
+{
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+        const bf16x8 b = cat(x.h, x.l);
+        return mma32(cat(yt.l, yt.l), b, mma32(cat(yt.h, yt.h), b, zero));
+    } else {
+        f32x4 r = zero;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) r = mma4(yt.x[s], x.x[s], r);
+        return r;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // helper wave: A, P and T = (I + A)^{-1} Diag(beta) for one chunk
+//
+// A is strictly lower triangular, so A^16 = 0 and
+//   (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
+// exactly (each factor pair telescopes: (I + A)(I - A) = I - A^2, ...).  The
+// factors are polynomials in A and commute; the inverse is formed with
+// eight 16x16 matrix-core products, keeping every intermediate in registers.
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
+__device__ __forceinline__ void helper(Buf<C> &B, int lane)
 {
     using OT = typename C::OT;
+    typedef OT OT4 __attribute__((ext_vector_type(4)));
+    constexpr bool BF = C::BF;
     const int j = lane & 15, g4 = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // at[e] (lane (j, g4)) = -(KE_j . Kd_{4 g4 + e})           (A before beta)
-    // pt[e] (lane (j, g4)) =   QE_j . Kd_{4 g4 + e} = P[j][4 g4 + e]
-    // Operands are ordered so that each lane ends up holding a row segment
-    // (row j, columns 4 g4 .. 4 g4 + 3), which it writes as one vector.
-    f32x4 at = zero, pt = zero;
-    if constexpr (C::BF) {
-        f32x4 p2 = zero, p3 = zero;               // three independent chains
+    // With M = KE Kd^T (M[t][s] = KE_t . Kd_s):
+    //   mt[e] (lane (j, g4)) = -M[j][4 g4 + e]       (D layout of -M^T)
+    //   mc[e] (lane (j, g4)) = -M[4 g4 + e][j]       (D layout of -M)
+    //   pt[e] (lane (j, g4)) =  QE_j . Kd_{4 g4 + e} = P[j][4 g4 + e]
+    f32x4 mt = zero, mc = zero, pt = zero;
+    if constexpr (BF) {
+        f32x4 p2 = zero, p3 = zero;
         if constexpr (C::DK >= 32) {
             // K slot (g4, i) = channel 32 s + 8 g4 + i on both operands
 #pragma unroll
@@ -386,7 +433,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
                 const bf16x8 nk = ld8b(&B.NK[j][kk]);
                 const bf16x8 qh = ld8b(&B.QH[j][kk]), ql = ld8b(&B.QL[j][kk]);
                 const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
-                at = mma32(dh, nk, at);
+                mt = mma32(dh, nk, mt);
+                mc = mma32(nk, dh, mc);
                 pt = mma32(dh, qh, pt);
                 p2 = mma32(dl, qh, p2);
                 p3 = mma32(dh, ql, p3);
@@ -400,7 +448,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
             const bf16x4 dh = ld4b(&B.DH[j][kk]);
             const bf16x8 dd = cat(dh, ld4b(&B.DL[j][kk]));
             const bf16x4 z = {};
-            at = mma32(cat(dh, z), cat(nk, z), at);
+            mt = mma32(cat(dh, z), cat(nk, z), mt);
+            mc = mma32(cat(nk, z), cat(dh, z), mc);
             pt = mma32(dd, cat(qh, qh), pt);    // (dh + dl) qh
             p2 = mma32(dd, cat(ql, ql), p2);    // (dh + dl) ql
         }
@@ -409,17 +458,17 @@ __device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
 #pragma unroll 8
         for (int s = 0; s < C::DK / 4; ++s) {
             const int kk = 4 * s + g4;
-            at = mma4(B.DH[j][kk], B.NK[j][kk], at);
+            mt = mma4(B.DH[j][kk], B.NK[j][kk], mt);
+            mc = mma4(B.NK[j][kk], B.DH[j][kk], mc);
             pt = mma4(B.DH[j][kk], B.QH[j][kk], pt);
         }
     }
-    typedef OT OT4 __attribute__((ext_vector_type(4)));
+    // P row j (lower triangle including the diagonal)
     {
-        // P row j (lower triangle including the diagonal)
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e <= j) ? pt[e] : 0.f;
-        if constexpr (C::BF) {
+        if constexpr (BF) {
             const bf16x4 h = {f2bf(pv[0]), f2bf(pv[1]), f2bf(pv[2]), f2bf(pv[3])};
             *reinterpret_cast<bf16x4 *>(&B.PH[j][4 * g4]) = h;
             *reinterpret_cast<bf16x4 *>(&B.PL[j][4 * g4]) =
@@ -428,59 +477,43 @@ __device__ __forceinline__ void helper(Buf<C> &B, float (*AF)[20], int lane)
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
-        // A row j: A_{jc} = beta_j KE_j . Kd_c for c < j (NK = -KE)
-        const float bj = B.BETA[j];
-        f32x4 av;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) av[e] = (4 * g4 + e < j) ? -bj * at[e] : 0.f;
-        *reinterpret_cast<f32x4 *>(&AF[j][4 * g4]) = av;
     }
-    // make this wave's AF writes visible to its own later reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Row j of T' = (I + A)^{-1} from T' (I + A) = I, right-looking: once
-    // T'_{j,i} is final (i from 15 down), it is removed from every column
-    // c < i.  The critical path is one FMA per column; row i of A is read
-    // from LDS as a broadcast (every lane reads the same address).  Every
-    // lane runs row lane % 16; lanes 0..15 write it.
-    float acc[16];
+    // A[t][s] = beta_t M[t][s] (s < t), in D layout (a) and transposed (at)
+    const float bj = B.BETA[j];
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.BETA[4 * g4]);
+    f32x4 a, at, id;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = (c == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 15; i >= 1; --i) {
-        const float ti = acc[i];
-#pragma unroll
-        for (int c4 = 0; c4 < i; c4 += 4) {
-            const f32x4 ar = *reinterpret_cast<const f32x4 *>(&AF[i][c4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (c4 + e < i) acc[c4 + e] = __builtin_fmaf(-ar[e], ti, acc[c4 + e]);
-        }
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        a[e] = (r > j) ? -b4[e] * mc[e] : 0.f;      // A[r][j]
+        at[e] = (r < j) ? -bj * mt[e] : 0.f;        // A[j][r]
+        id[e] = (r == j) ? 1.f : 0.f;
     }
-    if (lane < 16) {
-        // T = T' Diag(beta): column c scaled by beta_c
-        float tv[16];
-#pragma unroll
-        for (int c4 = 0; c4 < 16; c4 += 4) {
-            const f32x4 bb = *reinterpret_cast<const f32x4 *>(&B.BETA[c4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) tv[c4 + e] = acc[c4 + e] * bb[e];
-        }
-#pragma unroll
-        for (int c0 = 0; c0 < 16; c0 += 4) {
-            if constexpr (C::BF) {
-                const bf16x4 h = {f2bf(tv[c0]), f2bf(tv[c0 + 1]), f2bf(tv[c0 + 2]),
-                                  f2bf(tv[c0 + 3])};
-                *reinterpret_cast<bf16x4 *>(&B.TH[j][c0]) = h;
-                *reinterpret_cast<bf16x4 *>(&B.TL[j][c0]) =
-                    bf16x4{f2bf(tv[c0] - bf2f(h[0])), f2bf(tv[c0 + 1] - bf2f(h[1])),
-                           f2bf(tv[c0 + 2] - bf2f(h[2])), f2bf(tv[c0 + 3] - bf2f(h[3]))};
-            } else {
-                *reinterpret_cast<OT4 *>(&B.TH[j][c0]) =
-                    OT4{tv[c0], tv[c0 + 1], tv[c0 + 2], tv[c0 + 3]};
-            }
-        }
+    const Tile<BF> tA = to_tile<BF>(a), tAT = to_tile<BF>(at);
+    const f32x4 a2 = prod<BF>(tAT, tA);             // A^2
+    const f32x4 a2t = prod<BF>(tA, tAT);            // (A^2)^T
+    const Tile<BF> tA2 = to_tile<BF>(a2), tA2T = to_tile<BF>(a2t);
+    const f32x4 a4 = prod<BF>(tA2T, tA2);           // A^4
+    const f32x4 a4t = prod<BF>(tA2, tA2T);          // (A^4)^T
+    // Y1^T = ((I - A)(I + A^2))^T = I - A^T + (A^2)^T - (A^2)^T A^T
+    const f32x4 y1t = id - at + a2t - prod<BF>(tA2, tAT);
+    const Tile<BF> tA4 = to_tile<BF>(a4), tA4T = to_tile<BF>(a4t);
+    const f32x4 a8 = prod<BF>(tA4T, tA4);           // A^8
+    // Y2^T = (Y1 (I + A^4))^T = Y1^T + (A^4)^T Y1^T
+    const Tile<BF> tY1T = to_tile<BF>(y1t);
+    const f32x4 y2t = y1t + prod<BF>(tA4, tY1T);
+    // (I + A)^{-T} = Y2^T + (A^8)^T Y2^T: lane (j, g4) holds row j of the
+    // inverse, columns 4 g4 .. 4 g4 + 3
+    const Tile<BF> tA8 = to_tile<BF>(a8), tY2T = to_tile<BF>(y2t);
+    const f32x4 tinv = y2t + prod<BF>(tA8, tY2T);
+    // T = (I + A)^{-1} Diag(beta): column 4 g4 + e scaled by beta_{4 g4 + e}
+    const f32x4 tv = tinv * b4;
+    if constexpr (BF) {
+        const bf16x4 h = to_bf4(tv);
+        *reinterpret_cast<bf16x4 *>(&B.TH[j][4 * g4]) = h;
+        *reinterpret_cast<bf16x4 *>(&B.TL[j][4 * g4]) = to_bf4(tv - from_bf4(h));
+    } else {
+        *reinterpret_cast<OT4 *>(&B.TH[j][4 * g4]) = OT4{tv[0], tv[1], tv[2], tv[3]};
     }
 }
 
@@ -585,7 +618,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
 // the kernel
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
-__global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF>::NT), (NBUF == 2 ? 3 : 1))
+__global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF>::NT), 1)
 void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                         const TI *__restrict__ v, const float *__restrict__ g,
                         const float *__restrict__ beta, const float *__restrict__ S0,
@@ -626,83 +659,100 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool is_helper = wave == NW;
+    // roles: consumer waves 0 .. NW-1, builder waves NW .. 2NW-1, one helper
+    const bool is_cons = wave < NW;
+    const bool is_build = !is_cons && wave < 2 * NW;
+    const int bw = wave - NW, btid = tid - C::NC;     // builder wave / thread index
     const int j = lane & 15, g4 = lane >> 4;
 
-    // consumer state: S[:, col_base + 16 wave + j], rows 16 t + 4 g4 + i
-    f32x4 S[DK / 16];
-    const int64_t sbase = (int64_t)chain * DK * DV + col_base + 16 * wave + j;
-    if (!is_helper) {
+    auto ntok_of = [&](int cc) -> int {
+        const int64_t rem = T - 16 * (int64_t)cc;
+        return (int)(rem < 0 ? 0 : (rem < 16 ? rem : 16));
+    };
+
+    // Pipeline over chunks with a ring of NBUF = 3 operand slots, in phases
+    // separated by barriers (every role passes the same nch + 2 barriers):
+    //   phase 0       builders build chunks 0 and 1
+    //   phase 1       helper forms A, P, T of chunk 0
+    //   phase 2 + c   builders build chunk c + 2 (slot (c + 2) % 3), helper
+    //                 forms A, P, T of chunk c + 1 (slot (c + 1) % 3),
+    //                 consumers store O of chunk c - 1 and run the S chain
+    //                 of chunk c (slot c % 3)
+    // Each SIMD holds one consumer and one builder wave, so the builder's
+    // VALU work fills the consumer's matrix-core and LDS waits.  Every role
+    // runs its own loop; the role is wave-uniform.
+    static_assert(NBUF == 3 && LAG == 2, "phase plan");
+    if (is_build) {
+        // Loads are issued unconditionally: buffer resources of chunks past
+        // the end are empty and read zeros.  A chunk's raw registers are
+        // loaded right after the previous build, one phase before use.
+        Raw<C> raw;
+        auto load = [&](int cc) {
+            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
+                        col_base, bw, lane, btid);
+        };
+        load(0);
+        if (nch > 0) build<C>(sm.buf[0], raw, bw, lane, btid);
+        load(1);
+        if (nch > 1) build<C>(sm.buf[1], raw, bw, lane, btid);
+        load(2);
+        __syncthreads();
+        __syncthreads();
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            if (c + 2 < nch) build<C>(sm.buf[(c + 2) % 3], raw, bw, lane, btid);
+            load(c + 3);
+            __syncthreads();
+        }
+    } else if (!is_cons) {
+        __syncthreads();
+        if (nch > 0) helper<C>(sm.buf[0], lane);
+        __syncthreads();
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) helper<C>(sm.buf[(c + 1) % 3], lane);
+            __syncthreads();
+        }
+    } else {
+        // consumer state: S[:, col_base + 16 wave + j], rows 16 t + 4 g4 + i
+        f32x4 S[DK / 16];
+        const int64_t sbase = (int64_t)chain * DK * DV + col_base + 16 * wave + j;
 #pragma unroll
         for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[t][i] = S0 ? S0[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] : 0.f;
-    }
-
-    // Prologue: build the first LAG chunks (and form A, P, T of chunk 0).
-    // Main loop, chunk c: build chunk c + LAG, load chunk c + LAG + 1,
-    // consume chunk c, form A, P, T of chunk c + 1.  Every global load and
-    // store of the main loop is issued unconditionally (buffer resources of
-    // chunks past the end are empty), so the compiler's memory-counter waits
-    // before a build cover exactly the loads that build needs.
-    Raw<C> raw;
-    auto ntok_of = [&](int cc) -> int {
-        const int64_t rem = T - 16 * (int64_t)cc;
-        return (int)(rem < 0 ? 0 : (rem < 16 ? rem : 16));
-    };
-    if (!is_helper)
-        load_raw<C>(raw, q, k, v, g, beta, bos, ntok_of(0), H, h, DV, col_base, wave, lane, tid);
-#pragma unroll 1
-    for (int c = -LAG; c < 0; ++c) {
-        if (!is_helper) {
-            if (c + LAG < nch) build<C>(sm.buf[c + LAG], raw, wave, lane, tid);
-            const int cl = c + LAG + 1;
-            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cl, ntok_of(cl), H, h, DV,
-                        col_base, wave, lane, tid);
-        }
-        if constexpr (NBUF == 2) __syncthreads();
-        if (is_helper && c + 1 == 0 && nch > 0) helper<C>(sm.buf[0], sm.AF, lane);
-        __syncthreads();
-    }
-    // O of chunk c is written at the start of iteration c + 1, before that
-    // iteration's loads: the stores are then older than the loads the next
-    // build waits for, so that wait never includes store acknowledgements.
-    const int64_t rowo = (int64_t)H * DV;
-    const int ooff = (int)(h * DV + col_base + 16 * wave + j);
-    f32x4 ov = {0.f, 0.f, 0.f, 0.f};
-    auto store_o = [&](int cc) {
-        const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
-                                    (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int64_t)sizeof(TO));
+        // O of chunk c is written at the start of iteration c + 1, so the
+        // stores overlap the next chain instead of delaying this one.
+        const int64_t rowo = (int64_t)H * DV;
+        int ooff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            bstore(ro, (int)(((4 * g4 + i) * rowo + ooff) * sizeof(TO)), (TO)ov[i]);
-    };
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-        if (!is_helper) {
-            const int cb = c + LAG;
-            if (cb < nch) build<C>(sm.buf[cb % NBUF], raw, wave, lane, tid);
-            store_o(c - 1);
-            const int cl = cb + 1;
-            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cl, ntok_of(cl), H, h, DV,
-                        col_base, wave, lane, tid);
-        }
-        if constexpr (NBUF == 2) __syncthreads();
-        if (!is_helper) {
-            ov = consume<C>(sm.buf[c % NBUF], S, wave, lane);
-        } else {
-            if (c + 1 < nch) helper<C>(sm.buf[(c + 1) % NBUF], sm.AF, lane);
-        }
+            ooff[i] = (int)(((4 * g4 + i) * rowo + h * DV + col_base + 16 * wave + j) *
+                            sizeof(TO));
+        f32x4 ov = {0.f, 0.f, 0.f, 0.f};
+        auto store_o = [&](int cc) {
+            const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
+                                        (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int64_t)sizeof(TO));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bstore(ro, ooff[i], (TO)ov[i]);
+        };
         __syncthreads();
-    }
-    if (!is_helper && nch > 0) store_o(nch - 1);
-    if (!is_helper && S_T) {
+        __syncthreads();
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            store_o(c - 1);
+            ov = consume<C>(sm.buf[c % 3], S, wave, lane);
+            __syncthreads();
+        }
+        if (nch > 0) store_o(nch - 1);
+        if (S_T) {
 #pragma unroll
-        for (int t = 0; t < DK / 16; ++t)
+            for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S_T[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
+                for (int i = 0; i < 4; ++i)
+                    S_T[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
+        }
     }
 }
 
@@ -732,11 +782,6 @@ struct PickNW {
     static constexpr int value = byv < bydk ? byv : bydk;
 };
 
-// Ring depth: with more workgroups than CUs, the two-deep ring (small enough
-// for two workgroups per CU) lets one workgroup run while the other waits at
-// a barrier; otherwise the three-deep ring needs one barrier per chunk.
-constexpr int64_t kNumCUs = 256;
-
 template <typename TI, typename TO, int DK, int DV>
 static hipError_t launch_dims(const PrefillArgs &a)
 {
@@ -745,8 +790,8 @@ static hipError_t launch_dims(const PrefillArgs &a)
     const int64_t chains = (int64_t)a.n_seqs * a.H;
     if (chains == 0) return hipSuccess;
     if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
-    constexpr bool two_fit = sizeof(Smem<Cfg<TI, DK, NW, 2>>) <= 80 * 1024;
-    if (two_fit && chains * NB > kNumCUs) return launch_t<TI, TO, DK, DV, NW, 2>(a, chains);
+    static_assert(sizeof(Smem<Cfg<TI, DK, NW, 3>>) <= 160 * 1024, "LDS");
+    (void)NB;
     return launch_t<TI, TO, DK, DV, NW, 3>(a, chains);
 }
 
