@@ -73,13 +73,28 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b)
 }
 __device__ __forceinline__ bf16x4 ld4b(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 __device__ __forceinline__ bf16x8 ld8b(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-__device__ __forceinline__ bf16x4 to_bf4(f32x4 x)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Two floats as packed bf16 words h = RNE(x) and l = RNE(x - h): one packed
+// conversion each, with h brought back to fp32 by a shift and a mask.
+__device__ __forceinline__ void split2(float a, float b, uint32_t &h, uint32_t &l)
 {
-    return bf16x4{f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
+    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+    l = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
 }
-__device__ __forceinline__ f32x4 from_bf4(bf16x4 x)
+__device__ __forceinline__ uint32_t pack2(float a, float b)
 {
-    return f32x4{bf2f(x[0]), bf2f(x[1]), bf2f(x[2]), bf2f(x[3])};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &h, bf16x4 &l)
+{
+    uint32_t h0, l0, h1, l1;
+    split2(x[0], x[1], h0, l0);
+    split2(x[2], x[3], h1, l1);
+    h = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+    l = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
 }
 __device__ __forceinline__ int64_t uniform64(int64_t x)
 {
@@ -95,8 +110,8 @@ __device__ __forceinline__ float bcast(float x, int lane)
 // hi/lo split of a D-layout tile packed as 32-deep B operands [hi; hi], [lo; lo]
 __device__ __forceinline__ void split_hl(f32x4 x, bf16x8 &hh, bf16x8 &ll)
 {
-    const bf16x4 h = to_bf4(x);
-    const bf16x4 l = to_bf4(x - from_bf4(h));
+    bf16x4 h, l;
+    split4(x, h, l);
     hh = cat(h, h);
     ll = cat(l, l);
 }
@@ -116,8 +131,6 @@ __device__ __forceinline__ uint32_t bload32(rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x2 bload64(rsrc_t r, int off)
 {
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -301,20 +314,21 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         const float f0 = fast_exp2(-d0), f1 = fast_exp2(-d1);         // 1 / E
         const float ka = elem<C>(r.k[t], 0), kb = elem<C>(r.k[t], 1);
         const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
-        *reinterpret_cast<OT2 *>(&B.NK[tok][ch]) = OT2{(OT)(-ka * e0), (OT)(-kb * e1)};
         const float qe0 = qa * e0, qe1 = qb * e1;
         const float kd0 = ka * f0, kd1 = kb * f1;
         if constexpr (C::BF) {
-            const bf16 qh0 = f2bf(qe0), qh1 = f2bf(qe1);
-            const bf16 dh0 = f2bf(kd0), dh1 = f2bf(kd1);
-            const bf16 dl0 = f2bf(kd0 - bf2f(dh0)), dl1 = f2bf(kd1 - bf2f(dh1));
-            *reinterpret_cast<OT2 *>(&B.QH[tok][ch]) = OT2{qh0, qh1};
-            *reinterpret_cast<OT2 *>(&B.QL[tok][ch]) =
-                OT2{f2bf(qe0 - bf2f(qh0)), f2bf(qe1 - bf2f(qh1))};
-            *reinterpret_cast<OT2 *>(&B.DH[tok][ch]) = OT2{dh0, dh1};
-            *reinterpret_cast<OT2 *>(&B.DL[tok][ch]) = OT2{dl0, dl1};
-            kdh0[t] = dh0; kdh1[t] = dh1; kdl0[t] = dl0; kdl1[t] = dl1;
+            uint32_t qh, ql, dh, dl;
+            split2(qe0, qe1, qh, ql);
+            split2(kd0, kd1, dh, dl);
+            *reinterpret_cast<uint32_t *>(&B.NK[tok][ch]) = pack2(-ka * e0, -kb * e1);
+            *reinterpret_cast<uint32_t *>(&B.QH[tok][ch]) = qh;
+            *reinterpret_cast<uint32_t *>(&B.QL[tok][ch]) = ql;
+            *reinterpret_cast<uint32_t *>(&B.DH[tok][ch]) = dh;
+            *reinterpret_cast<uint32_t *>(&B.DL[tok][ch]) = dl;
+            const bf16x2 vh = __builtin_bit_cast(bf16x2, dh), vl = __builtin_bit_cast(bf16x2, dl);
+            kdh0[t] = vh[0]; kdh1[t] = vh[1]; kdl0[t] = vl[0]; kdl1[t] = vl[1];
         } else {
+            *reinterpret_cast<OT2 *>(&B.NK[tok][ch]) = OT2{-ka * e0, -kb * e1};
             *reinterpret_cast<OT2 *>(&B.QH[tok][ch]) = OT2{qe0, qe1};
             *reinterpret_cast<OT2 *>(&B.DH[tok][ch]) = OT2{kd0, kd1};
             kdh0[t] = kd0; kdh1[t] = kd1;
@@ -380,8 +394,9 @@ template <bool BF>
 __device__ __forceinline__ Tile<BF> to_tile(f32x4 x)
 {
     if constexpr (BF) {
-        const bf16x4 h = to_bf4(x);
-        return Tile<true>{h, to_bf4(x - from_bf4(h))};
+        Tile<true> t;
+        split4(x, t.h, t.l);
+        return t;
     } else {
         return Tile<false>{x};
     }
@@ -469,11 +484,10 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e <= j) ? pt[e] : 0.f;
         if constexpr (BF) {
-            const bf16x4 h = {f2bf(pv[0]), f2bf(pv[1]), f2bf(pv[2]), f2bf(pv[3])};
+            bf16x4 h, l;
+            split4(f32x4{pv[0], pv[1], pv[2], pv[3]}, h, l);
             *reinterpret_cast<bf16x4 *>(&B.PH[j][4 * g4]) = h;
-            *reinterpret_cast<bf16x4 *>(&B.PL[j][4 * g4]) =
-                bf16x4{f2bf(pv[0] - bf2f(h[0])), f2bf(pv[1] - bf2f(h[1])),
-                       f2bf(pv[2] - bf2f(h[2])), f2bf(pv[3] - bf2f(h[3]))};
+            *reinterpret_cast<bf16x4 *>(&B.PL[j][4 * g4]) = l;
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
@@ -509,9 +523,10 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     // T = (I + A)^{-1} Diag(beta): column 4 g4 + e scaled by beta_{4 g4 + e}
     const f32x4 tv = tinv * b4;
     if constexpr (BF) {
-        const bf16x4 h = to_bf4(tv);
+        bf16x4 h, l;
+        split4(tv, h, l);
         *reinterpret_cast<bf16x4 *>(&B.TH[j][4 * g4]) = h;
-        *reinterpret_cast<bf16x4 *>(&B.TL[j][4 * g4]) = to_bf4(tv - from_bf4(h));
+        *reinterpret_cast<bf16x4 *>(&B.TL[j][4 * g4]) = l;
     } else {
         *reinterpret_cast<OT4 *>(&B.TH[j][4 * g4]) = OT4{tv[0], tv[1], tv[2], tv[3]};
     }
@@ -544,10 +559,10 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             constexpr int NS = C::DK / 32;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const bf16x4 h0 = to_bf4(S[2 * s]), h1 = to_bf4(S[2 * s + 1]);
-                const bf16x8 sh = cat(h0, h1);
-                const bf16x8 sl = cat(to_bf4(S[2 * s] - from_bf4(h0)),
-                                      to_bf4(S[2 * s + 1] - from_bf4(h1)));
+                bf16x4 h0, l0, h1, l1;
+                split4(S[2 * s], h0, l0);
+                split4(S[2 * s + 1], h1, l1);
+                const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
                 const int kk = 32 * s + 4 * g4;
                 const bf16x8 nk = cat(ld4b(&B.NK[j][kk]), ld4b(&B.NK[j][kk + 16]));
                 const bf16x8 qh = cat(ld4b(&B.QH[j][kk]), ld4b(&B.QH[j][kk + 16]));
@@ -562,8 +577,8 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             o += o2 + o3;
         } else {
             // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
-            const bf16x4 hh = to_bf4(S[0]);
-            const bf16x4 ll = to_bf4(S[0] - from_bf4(hh));
+            bf16x4 hh, ll;
+            split4(S[0], hh, ll);
             const bf16x4 nk = ld4b(&B.NK[j][4 * g4]);
             const bf16x8 qq = cat(ld4b(&B.QH[j][4 * g4]), ld4b(&B.QL[j][4 * g4]));
             x = mma32(cat(nk, nk), cat(hh, ll), x);
@@ -684,26 +699,36 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     static_assert(NBUF == 3 && LAG == 2, "phase plan");
     if (is_build) {
         // Loads are issued unconditionally: buffer resources of chunks past
-        // the end are empty and read zeros.  A chunk's raw registers are
-        // loaded right after the previous build, one phase before use.
-        Raw<C> raw;
-        auto load = [&](int cc) {
-            load_raw<C>(raw, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
+        // the end are empty and read zeros.  Two register sets alternate
+        // (even chunks in ra, odd in rb), so a chunk's loads are issued two
+        // phases before its build.
+        Raw<C> ra, rb;
+        auto load = [&](Raw<C> &r, int cc) {
+            load_raw<C>(r, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
                         col_base, bw, lane, btid);
         };
-        load(0);
-        if (nch > 0) build<C>(sm.buf[0], raw, bw, lane, btid);
-        load(1);
-        if (nch > 1) build<C>(sm.buf[1], raw, bw, lane, btid);
-        load(2);
+        load(ra, 0);
+        load(rb, 1);
+        if (nch > 0) build<C>(sm.buf[0], ra, bw, lane, btid);
+        load(ra, 2);
+        if (nch > 1) build<C>(sm.buf[1], rb, bw, lane, btid);
+        load(rb, 3);
         __syncthreads();
         __syncthreads();
+        // (the odd last phase is peeled, so that every path back to the loop
+        // head has issued both register sets' loads in the same order and
+        // the compiler's counter waits let the newer set stay in flight)
+        int c = 0;
 #pragma unroll 1
-        for (int c = 0; c < nch; ++c) {
-            if (c + 2 < nch) build<C>(sm.buf[(c + 2) % 3], raw, bw, lane, btid);
-            load(c + 3);
+        for (; c + 1 < nch; c += 2) {
+            if (c + 2 < nch) build<C>(sm.buf[(c + 2) % 3], ra, bw, lane, btid);
+            load(ra, c + 4);
+            __syncthreads();
+            if (c + 3 < nch) build<C>(sm.buf[(c + 3) % 3], rb, bw, lane, btid);
+            load(rb, c + 5);
             __syncthreads();
         }
+        if (c < nch) __syncthreads();           // phase of the last chunk (odd nch)
     } else if (!is_cons) {
         __syncthreads();
         if (nch > 0) helper<C>(sm.buf[0], lane);
