@@ -162,7 +162,7 @@ struct Cfg {
     static constexpr int NT = (2 * NW + 1) * WAVE; // consumers, builders, helper
     static constexpr int NC = NW * WAVE;           // consumer (= builder) threads
     static constexpr int LDK = DK + (BF ? 8 : 4);  // row stride of [16][DK] arrays
-    static constexpr int LDT = 20;                 // row stride of Kd^T [DK][16]
+    static constexpr int LDT = BF ? 24 : 20;       // row stride of Kd^T [DK][16]
     static constexpr int LDP = BF ? 24 : 20;       // row stride of T, P [16][16]
     static constexpr int LDV = BV + (BF ? 8 : 4);
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
@@ -218,17 +218,6 @@ __device__ __forceinline__ float elem(typename Raw<C>::P2 x, int i)
     if constexpr (C::BF) return u16_to_f(i ? (uint16_t)(x >> 16) : (uint16_t)(x & 0xffffu));
     else return __uint_as_float(x[i]);
 }
-template <class C>
-__device__ __forceinline__ float elem4(typename Raw<C>::P4 x, int i)
-{
-    if constexpr (C::BF) {
-        const uint32_t w = x[i >> 1];
-        return u16_to_f((i & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffffu));
-    } else {
-        return __uint_as_float(x[i]);
-    }
-}
-
 // ---------------------------------------------------------------------------
 // loads of one chunk's raw inputs through buffer resources bounded by the
 // chunk's real tokens: padded tokens read k = q = v = 0, g = 0, beta = 0,
@@ -364,11 +353,9 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         B.DEC[ch + 1] = fast_exp2(T1);
     }
     {
+        // v is stored in its input type: the raw bits are copied
         const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-        typedef OT OT4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<OT4 *>(&B.V[row][4 * c4]) =
-            OT4{(OT)elem4<C>(r.v, 0), (OT)elem4<C>(r.v, 1), (OT)elem4<C>(r.v, 2),
-                (OT)elem4<C>(r.v, 3)};
+        *reinterpret_cast<typename Raw<C>::P4 *>(&B.V[row][4 * c4]) = r.v;
     }
     if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
 }
