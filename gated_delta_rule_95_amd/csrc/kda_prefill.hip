@@ -367,12 +367,12 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
 // the slots of group g; the left factor Y must then be given as Y^T in D
 // layout (lane (r, g) holds Y[r][4 g + i]).  So prod(YT, X) = Y X and
 // prod(X, YT) = X^T Y^T take the same two tiles with the roles swapped.
-// bf16: the tiles are hi/lo pairs and the product keeps all four terms,
-// [Yh | Yh] x [Xh ; Xl] + [Yl | Yl] x [Xh ; Xl].  fp32: four K=4 steps.
+// bf16: one product, the K slots 4..7 of each group hold zeros.  fp32: four
+// K=4 steps.
 // ---------------------------------------------------------------------------
 template <bool BF> struct Tile;
 template <> struct Tile<true> {
-    bf16x4 h, l;
+    bf16x8 v;                            // [X (4 slots) | 0]
 };
 template <> struct Tile<false> {
     f32x4 x;
@@ -381,9 +381,8 @@ template <bool BF>
 __device__ __forceinline__ Tile<BF> to_tile(f32x4 x)
 {
     if constexpr (BF) {
-        Tile<true> t;
-        split4(x, t.h, t.l);
-        return t;
+        const u32x2 h = {pack2(x[0], x[1]), pack2(x[2], x[3])};
+        return Tile<true>{cat(__builtin_bit_cast(bf16x4, h), bf16x4{})};
     } else {
         return Tile<false>{x};
     }
@@ -393,8 +392,7 @@ __device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
 {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (BF) {
-        const bf16x8 b = cat(x.h, x.l);
-        return mma32(cat(yt.l, yt.l), b, mma32(cat(yt.h, yt.h), b, zero));
+        return mma32(yt.v, x.v, zero);
     } else {
         f32x4 r = zero;
 #pragma unroll
@@ -411,6 +409,10 @@ __device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
 // exactly (each factor pair telescopes: (I + A)(I - A) = I - A^2, ...).  The
 // factors are polynomials in A and commute; the inverse is formed with
 // eight 16x16 matrix-core products, keeping every intermediate in registers.
+// With bf16 inputs A is itself formed from single-bf16 operands, and the
+// products of the inverse take single-bf16 operands too (checked in
+// emulation against the oracle: no change in the error of o or S_T); T is
+// then written as a hi/lo pair.
 // ---------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void helper(Buf<C> &B, int lane)
