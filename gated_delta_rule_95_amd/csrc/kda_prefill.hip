@@ -162,8 +162,12 @@ struct Cfg {
     static constexpr int NT = (2 * NW + 1) * WAVE; // consumers, builders, helper
     static constexpr int NC = NW * WAVE;           // consumer (= builder) threads
     static constexpr int LDK = DK + (BF ? 8 : 4);  // row stride of [16][DK] arrays
-    static constexpr int LDT = BF ? 24 : 20;       // row stride of Kd^T [DK][16]
-    static constexpr int LDP = BF ? 24 : 20;       // row stride of T, P [16][16]
+    // Kd^T, T and P rows: bf16 rows hold each group of four tokens as
+    // [4 hi | 4 lo], so one 16-byte read is an MFMA A operand; the 80-byte
+    // row stride keeps those reads and the builder's writes at the minimum
+    // LDS bank-conflict degree
+    static constexpr int LDT = BF ? 40 : 20;       // row stride of Kd^T [DK][16]
+    static constexpr int LDP = BF ? 40 : 20;       // row stride of T, P [16][16]
     static constexpr int LDV = BV + (BF ? 8 : 4);
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
     static constexpr int CW = DK / NW;
@@ -184,12 +188,9 @@ struct alignas(16) Buf {
     OT QL[C::LO ? 16 : 1][C::LDK];       // QE lo
     OT DH[16][C::LDK];                   // Kd hi                [token][channel]
     OT DL[C::LO ? 16 : 1][C::LDK];       // Kd lo
-    OT KH[C::DK][C::LDT];                // Kd^T hi              [channel][token]
-    OT KL[C::LO ? C::DK : 1][C::LDT];    // Kd^T lo
-    OT TH[16][C::LDP];                   // T hi                 [token r][token i]
-    OT TL[C::LO ? 16 : 1][C::LDP];
-    OT PH[16][C::LDP];                   // P hi
-    OT PL[C::LO ? 16 : 1][C::LDP];
+    OT KH[C::DK][C::LDT];                // Kd^T                 [channel][token]
+    OT TH[16][C::LDP];                   // T                    [token r][token i]
+    OT PH[16][C::LDP];                   // P
     OT V[16][C::LDV];                    // value block
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
@@ -323,15 +324,29 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
             kdh0[t] = kd0; kdh1[t] = kd1;
         }
     }
-    // Kd^T rows: this lane's TPG consecutive tokens of channels ch, ch + 1,
-    // written as vectors of (up to) four
-    if constexpr (TPG == 2) {
+    // Kd^T rows: this lane's TPG consecutive tokens of channels ch, ch + 1
+    if constexpr (C::BF) {
+        if constexpr (TPG == 2) {
+            const int o = 8 * (tok0 >> 2) + (tok0 & 3);
+            *reinterpret_cast<bf16x2 *>(&B.KH[ch][o]) = bf16x2{kdh0[0], kdh0[1]};
+            *reinterpret_cast<bf16x2 *>(&B.KH[ch][o + 4]) = bf16x2{kdl0[0], kdl0[1]};
+            *reinterpret_cast<bf16x2 *>(&B.KH[ch + 1][o]) = bf16x2{kdh1[0], kdh1[1]};
+            *reinterpret_cast<bf16x2 *>(&B.KH[ch + 1][o + 4]) = bf16x2{kdl1[0], kdl1[1]};
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPG; t += 4) {
+                const int o = 2 * (tok0 + t);
+                *reinterpret_cast<bf16x8 *>(&B.KH[ch][o]) =
+                    bf16x8{kdh0[t], kdh0[t + 1], kdh0[t + 2], kdh0[t + 3],
+                           kdl0[t], kdl0[t + 1], kdl0[t + 2], kdl0[t + 3]};
+                *reinterpret_cast<bf16x8 *>(&B.KH[ch + 1][o]) =
+                    bf16x8{kdh1[t], kdh1[t + 1], kdh1[t + 2], kdh1[t + 3],
+                           kdl1[t], kdl1[t + 1], kdl1[t + 2], kdl1[t + 3]};
+            }
+        }
+    } else if constexpr (TPG == 2) {
         *reinterpret_cast<OT2 *>(&B.KH[ch][tok0]) = OT2{kdh0[0], kdh0[1]};
         *reinterpret_cast<OT2 *>(&B.KH[ch + 1][tok0]) = OT2{kdh1[0], kdh1[1]};
-        if constexpr (C::BF) {
-            *reinterpret_cast<OT2 *>(&B.KL[ch][tok0]) = OT2{kdl0[0], kdl0[1]};
-            *reinterpret_cast<OT2 *>(&B.KL[ch + 1][tok0]) = OT2{kdl1[0], kdl1[1]};
-        }
     } else {
         typedef OT OT4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -340,12 +355,6 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
                 OT4{kdh0[t], kdh0[t + 1], kdh0[t + 2], kdh0[t + 3]};
             *reinterpret_cast<OT4 *>(&B.KH[ch + 1][tok0 + t]) =
                 OT4{kdh1[t], kdh1[t + 1], kdh1[t + 2], kdh1[t + 3]};
-            if constexpr (C::BF) {
-                *reinterpret_cast<OT4 *>(&B.KL[ch][tok0 + t]) =
-                    OT4{kdl0[t], kdl0[t + 1], kdl0[t + 2], kdl0[t + 3]};
-                *reinterpret_cast<OT4 *>(&B.KL[ch + 1][tok0 + t]) =
-                    OT4{kdl1[t], kdl1[t + 1], kdl1[t + 2], kdl1[t + 3]};
-            }
         }
     }
     if (tg == 0) {
@@ -475,8 +484,7 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
         if constexpr (BF) {
             bf16x4 h, l;
             split4(f32x4{pv[0], pv[1], pv[2], pv[3]}, h, l);
-            *reinterpret_cast<bf16x4 *>(&B.PH[j][4 * g4]) = h;
-            *reinterpret_cast<bf16x4 *>(&B.PL[j][4 * g4]) = l;
+            *reinterpret_cast<bf16x8 *>(&B.PH[j][8 * g4]) = cat(h, l);
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
@@ -514,8 +522,7 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     if constexpr (BF) {
         bf16x4 h, l;
         split4(tv, h, l);
-        *reinterpret_cast<bf16x4 *>(&B.TH[j][4 * g4]) = h;
-        *reinterpret_cast<bf16x4 *>(&B.TL[j][4 * g4]) = l;
+        *reinterpret_cast<bf16x8 *>(&B.TH[j][8 * g4]) = cat(h, l);
     } else {
         *reinterpret_cast<OT4 *>(&B.TH[j][4 * g4]) = OT4{tv[0], tv[1], tv[2], tv[3]};
     }
@@ -577,19 +584,18 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
         // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
         bf16x8 xhh, xll, uhh, ull;
         split_hl(x, xhh, xll);
-        const bf16x8 tt = cat(ld4b(&B.TH[j][4 * g4]), ld4b(&B.TL[j][4 * g4]));
+        const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
         u = mma32(tt, xhh, zero);
         u = mma32(tt, xll, u);
         split_hl(u, uhh, ull);
         // O += P U
-        const bf16x8 pp = cat(ld4b(&B.PH[j][4 * g4]), ld4b(&B.PL[j][4 * g4]));
+        const bf16x8 pp = ld8b(&B.PH[j][8 * g4]);
         o = mma32(pp, uhh, o);
         o = mma32(pp, ull, o);
         // S' = Sd + Kd^T U
 #pragma unroll
         for (int t = 0; t < C::DK / 16; ++t) {
-            const bf16x8 kd = cat(ld4b(&B.KH[16 * t + j][4 * g4]),
-                                  ld4b(&B.KL[16 * t + j][4 * g4]));
+            const bf16x8 kd = ld8b(&B.KH[16 * t + j][8 * g4]);
             S[t] = mma32(kd, uhh, S[t]);
             S[t] = mma32(kd, ull, S[t]);
         }
