@@ -102,8 +102,12 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     if ((s = check_dims(H, d_k, d_v)) != KDA_OK) return s;
     if (n_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "n_seqs must be >= 0 (got %d)", n_seqs);
     if (n_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens must be >= 0");
-    if (n_tokens >= (int64_t)1 << 31)
-        return fail(KDA_ERR_INVALID_ARG, "n_tokens must fit int32 (cu_seqlens is int32)");
+    if (n_tokens > ((int64_t)1 << 31) - 64)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "n_tokens must fit int32 with room for one chunk (cu_seqlens is int32)");
+    if ((int64_t)H * (d_k > d_v ? d_k : d_v) >= ((int64_t)1 << 25))
+        return fail(KDA_ERR_INVALID_ARG, "H * d must be below 2^25 (16 rows of a tensor "
+                                         "must stay below 2^31 bytes)");
     if (n_seqs == 0) {
         if (n_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens > 0 with n_seqs == 0");
         return ok();

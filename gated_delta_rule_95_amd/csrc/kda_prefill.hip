@@ -122,10 +122,13 @@ __device__ __forceinline__ void split_hl(f32x4 x, bf16x8 &hh, bf16x8 &ll)
 // store of the main loop is issued unconditionally).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;        // raw buffer, 32-bit data format
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
+// bytes >= 0; the host keeps 16 rows of any tensor below 2^31 bytes
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int bytes)
 {
-    const int n = bytes > 0 ? (int)bytes : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcFlags);
+    // the size is wave-uniform; readfirstlane keeps the resource in scalar
+    // registers whatever form the compiler gives the arithmetic before it
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), kRsrcFlags);
 }
 __device__ __forceinline__ uint32_t bload32(rsrc_t r, int off)
 {
@@ -233,17 +236,17 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
                                          int wave, int lane, int tid)
 {
     constexpr int ES = sizeof(TI);
-    const int64_t rowk = (int64_t)H * C::DK, rowv = (int64_t)H * DV;
+    const int rowk = H * C::DK, rowv = H * DV;
     const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * ES);
     const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * ES);
     const rsrc_t rg = make_rsrc(g + tok_base * rowk, ntok * rowk * 4);
     const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok * rowv * ES);
-    const rsrc_t rb = make_rsrc(beta + tok_base * H, (int64_t)ntok * H * 4);
+    const rsrc_t rb = make_rsrc(beta + tok_base * H, ntok * H * 4);
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
 #pragma unroll
     for (int t = 0; t < C::TPG; ++t) {
-        const int e = (tg * C::TPG + t) * (int)rowk + h * C::DK + ch;
+        const int e = (tg * C::TPG + t) * rowk + h * C::DK + ch;
         if constexpr (C::BF) {
             r.q[t] = bload32(rq, e * ES);
             r.k[t] = bload32(rk, e * ES);
@@ -254,7 +257,7 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
         r.g[t] = bload64(rg, e * 4);
     }
     const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-    const int ev = row * (int)rowv + h * DV + col_base + 4 * c4;
+    const int ev = row * rowv + h * DV + col_base + 4 * c4;
     if constexpr (C::BF) r.v = bload64(rv, ev * ES);
     else r.v = bload128(rv, ev * ES);
     r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
@@ -663,8 +666,8 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     // branches on them are scalar and the buffer resources built from them
     // live in scalar registers
     bos = uniform64(bos);
-    T = uniform64(T);
-    const int nch = (int)((T + 15) / 16);
+    const int Tn = __builtin_amdgcn_readfirstlane((int)T);     // < 2^31 - 64 (host)
+    const int nch = (Tn + 15) / 16;
     const int col_base = vb * C::BV;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -676,9 +679,13 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     const int j = lane & 15, g4 = lane >> 4;
 
     auto ntok_of = [&](int cc) -> int {
-        const int64_t rem = T - 16 * (int64_t)cc;
-        return (int)(rem < 0 ? 0 : (rem < 16 ? rem : 16));
+        const int rem = Tn - 16 * cc;
+        return rem < 0 ? 0 : (rem < 16 ? rem : 16);
     };
+    // Ring slot s.  The slot offset goes through readfirstlane, so every LDS
+    // address is formed as (uniform slot base + per-lane offset + constant)
+    // rather than carried as one pointer per access pattern across the loop.
+    auto slot = [&](int s) -> Buf<C> & { return sm.buf[__builtin_amdgcn_readfirstlane(s)]; };
 
     // Pipeline over chunks with a ring of NBUF = 3 operand slots, in phases
     // separated by barriers (every role passes the same nch + 2 barriers):
@@ -716,10 +723,10 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         int c = 0;
 #pragma unroll 1
         for (; c + 1 < nch; c += 2) {
-            if (c + 2 < nch) build<C>(sm.buf[(c + 2) % 3], ra, bw, lane, btid);
+            if (c + 2 < nch) build<C>(slot((c + 2) % 3), ra, bw, lane, btid);
             load(ra, c + 4);
             __syncthreads();
-            if (c + 3 < nch) build<C>(sm.buf[(c + 3) % 3], rb, bw, lane, btid);
+            if (c + 3 < nch) build<C>(slot((c + 3) % 3), rb, bw, lane, btid);
             load(rb, c + 5);
             __syncthreads();
         }
@@ -730,7 +737,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         __syncthreads();
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) helper<C>(sm.buf[(c + 1) % 3], lane);
+            if (c + 1 < nch) helper<C>(slot((c + 1) % 3), lane);
             __syncthreads();
         }
     } else {
@@ -744,7 +751,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
                 S[t][i] = S0 ? S0[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] : 0.f;
         // O of chunk c is written at the start of iteration c + 1, so the
         // stores overlap the next chain instead of delaying this one.
-        const int64_t rowo = (int64_t)H * DV;
+        const int rowo = H * DV;
         int ooff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -753,7 +760,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         f32x4 ov = {0.f, 0.f, 0.f, 0.f};
         auto store_o = [&](int cc) {
             const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
-                                        (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int64_t)sizeof(TO));
+                                        (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int)sizeof(TO));
 #pragma unroll
             for (int i = 0; i < 4; ++i) bstore(ro, ooff[i], (TO)ov[i]);
         };
@@ -762,7 +769,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             store_o(c - 1);
-            ov = consume<C>(sm.buf[c % 3], S, wave, lane);
+            ov = consume<C>(slot(c % 3), S, wave, lane);
             __syncthreads();
         }
         if (nch > 0) store_o(nch - 1);

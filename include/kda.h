@@ -105,8 +105,8 @@ typedef void *kda_stream_t;
  *   S0                 float32 entry states or NULL
  *   cu_seqlens         int32 device array or NULL (equal lengths)
  *   n_seqs             number of sequences, >= 0 (0: nothing is done)
- *   n_tokens           total tokens, >= 0
- *   H                  heads, >= 1
+ *   n_tokens           total tokens, 0 <= n_tokens <= 2^31 - 64
+ *   H                  heads, >= 1, with H * max(d_k, d_v) < 2^25
  *   d_k, d_v           16, 32, 64 or 128 each
  *   in_dtype           KDA_BF16 or KDA_F32 (q, k, v)
  *   out_dtype          dtype of o: KDA_BF16 (bf16 inputs only) or KDA_F32;

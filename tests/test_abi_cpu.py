@@ -67,6 +67,8 @@ def fwd(lib, **kw):
     (dict(n_seqs=0, n_tokens=5), 1, "n_seqs == 0"),
     (dict(o=P * 2), 1, "overlaps"),
     (dict(n_tokens=1 << 31, n_seqs=1), 1, "int32"),
+    (dict(n_tokens=(1 << 31) - 32, n_seqs=1), 1, "int32"),
+    (dict(H=1 << 18, dk=128, dv=128, n_tokens=0, n_seqs=1), 1, "2^25"),
 ])
 def test_fwd_validation(lib, kw, status, msg):
     assert fwd(lib, **kw) == status
