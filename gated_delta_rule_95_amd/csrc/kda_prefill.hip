@@ -440,7 +440,6 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     //   pt[e] (lane (j, g4)) =  QE_j . Kd_{4 g4 + e} = P[j][4 g4 + e]
     f32x4 mt = zero, mc = zero, pt = zero;
     if constexpr (BF) {
-        f32x4 p2 = zero, p3 = zero;
         if constexpr (C::DK >= 32) {
             // K slot (g4, i) = channel 32 s + 8 g4 + i on both operands
 #pragma unroll
@@ -452,8 +451,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
                 mt = mma32(dh, nk, mt);
                 mc = mma32(nk, dh, mc);
                 pt = mma32(dh, qh, pt);
-                p2 = mma32(dl, qh, p2);
-                p3 = mma32(dh, ql, p3);
+                pt = mma32(dl, qh, pt);
+                pt = mma32(dh, ql, pt);
             }
         } else {
             // d_k = 16: K slot (g4, i) = channel 4 g4 + i%4 of the hi (i < 4)
@@ -467,9 +466,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
             mt = mma32(cat(dh, z), cat(nk, z), mt);
             mc = mma32(cat(nk, z), cat(dh, z), mc);
             pt = mma32(dd, cat(qh, qh), pt);    // (dh + dl) qh
-            p2 = mma32(dd, cat(ql, ql), p2);    // (dh + dl) ql
+            pt = mma32(dd, cat(ql, ql), pt);    // (dh + dl) ql
         }
-        pt += p2 + p3;
     } else {
 #pragma unroll 8
         for (int s = 0; s < C::DK / 4; ++s) {
@@ -541,7 +539,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     const int j = lane & 15, g4 = lane >> 4;
     const int vc = 16 * wave + j;           // column inside the block
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 x, u, o = zero, x2 = zero, o2 = zero, o3 = zero;
+    f32x4 x, u, o = zero;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)B.V[4 * g4 + i][vc];
     // Sd = Diag(e^{Gc_16}) S
@@ -567,13 +565,11 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 const bf16x8 qh = cat(ld4b(&B.QH[j][kk]), ld4b(&B.QH[j][kk + 16]));
                 const bf16x8 ql = cat(ld4b(&B.QL[j][kk]), ld4b(&B.QL[j][kk + 16]));
                 x = mma32(nk, sh, x);
-                x2 = mma32(nk, sl, x2);
+                x = mma32(nk, sl, x);
                 o = mma32(qh, sh, o);            // QE Sd: the lo x lo term
-                o2 = mma32(qh, sl, o2);          // (2^-18) is dropped
-                o3 = mma32(ql, sh, o3);
+                o = mma32(qh, sl, o);            // (2^-18) is dropped
+                o = mma32(ql, sh, o);
             }
-            x += x2;
-            o += o2 + o3;
         } else {
             // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
             bf16x4 hh, ll;
