@@ -13,6 +13,8 @@
 // read once and written once), so it is built for HBM bandwidth: one
 // workgroup per (n, h); each thread owns 4 consecutive columns of R rows
 // and issues all of its R 16-byte state loads before doing anything else.
+// State loads and stores are nontemporal: the state is touched once per
+// step, so keeping it out of the caches leaves them to the small vectors.
 // Both column reductions (S'^T k and S'^T q) share one pass over the rows
 // and one LDS exchange; the o = S'^T q + u (k . q) identity removes the
 // second pass the read would otherwise need.
@@ -49,7 +51,8 @@ void kda_decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     f32x4 s[Sh::R];
 #pragma unroll
     for (int p = 0; p < Sh::R; ++p)
-        s[p] = *reinterpret_cast<const f32x4 *>(Sh_ + (r0 + p * Sh::RP) * DV + 4 * cb);
+        s[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4 *>(Sh_ + (r0 + p * Sh::RP) * DV + 4 * cb));
 
     // 2. per-channel vectors into LDS
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
@@ -96,7 +99,8 @@ void kda_decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     for (int p = 0; p < Sh::R; ++p) {
         const int i = r0 + p * Sh::RP;
         const float ki = s_k[i];
-        *reinterpret_cast<f32x4 *>(Sh_ + i * DV + 4 * cb) = s[p] + ki * u;
+        __builtin_nontemporal_store(s[p] + ki * u,
+                                    reinterpret_cast<f32x4 *>(Sh_ + i * DV + 4 * cb));
     }
     if (r0 == 0) Elem<TO>::st4(o + nh * DV + 4 * cb, qs + u * kqt);
 }
