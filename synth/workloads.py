@@ -165,11 +165,10 @@ def head_inputs(wl: Workload, n: int, h: int, T: int) -> Dict[str, np.ndarray]:
     if wl.stress:
         mask = _rng(wl, n, 0xFFFF, _BMASK).random(T) < 0.1
         beta = np.where(mask, np.float32(1.0), beta).astype(np.float32)
-        # repeat keys inside every 16-token tile aligned to the sequence start
-        for base in range(0, T, 16):
-            for j in range(8):
-                if base + j + 8 < T:
-                    k[base + j + 8] = k[base + j]
+        # repeat keys inside every 16-token tile aligned to the sequence start:
+        # position p with p % 16 >= 8 takes the key of p - 8
+        dst = np.nonzero(np.arange(T) % 16 >= 8)[0]
+        k[dst] = k[dst - 8]
     out = {"q": _maybe_bf16(wl, q), "k": _maybe_bf16(wl, k),
            "v": _maybe_bf16(wl, v), "g": g.astype(np.float32),
            "beta": beta.astype(np.float32)}
