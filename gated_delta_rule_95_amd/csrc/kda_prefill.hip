@@ -150,6 +150,16 @@ __device__ __forceinline__ void bstore(rsrc_t r, int off, float x)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, 0);
 }
+// four consecutive elements in the output type
+__device__ __forceinline__ void bstore4(rsrc_t r, int off, f32x4 x, bf16)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])}, r, off,
+                                          0, 0);
+}
+__device__ __forceinline__ void bstore4(rsrc_t r, int off, f32x4 x, float)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // configuration
@@ -170,7 +180,10 @@ struct Cfg {
     // row stride keeps those reads and the builder's writes at the minimum
     // LDS bank-conflict degree
     static constexpr int LDT = BF ? 40 : 20;       // row stride of Kd^T [DK][16]
-    static constexpr int LDP = BF ? 40 : 20;       // row stride of T, P [16][16]
+    static constexpr int LDP = BF ? 40 : 20;       // row stride of T [16][16]
+    // P rows (bf16): each group of four tokens as [4 hi | 4 hi | 4 lo | 4 lo]
+    // (B operands of the transposed output product), 144-byte stride
+    static constexpr int LDQ = BF ? 72 : 20;
     static constexpr int LDV = BV + (BF ? 8 : 4);
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
     static constexpr int CW = DK / NW;
@@ -193,7 +206,7 @@ struct alignas(16) Buf {
     OT DL[C::LO ? 16 : 1][C::LDK];       // Kd lo
     OT KH[C::DK][C::LDT];                // Kd^T                 [channel][token]
     OT TH[16][C::LDP];                   // T                    [token r][token i]
-    OT PH[16][C::LDP];                   // P
+    OT PH[16][C::LDQ];                   // P
     OT V[16][C::LDV];                    // value block
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
@@ -485,7 +498,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
         if constexpr (BF) {
             bf16x4 h, l;
             split4(f32x4{pv[0], pv[1], pv[2], pv[3]}, h, l);
-            *reinterpret_cast<bf16x8 *>(&B.PH[j][8 * g4]) = cat(h, l);
+            *reinterpret_cast<bf16x8 *>(&B.PH[j][16 * g4]) = cat(h, h);
+            *reinterpret_cast<bf16x8 *>(&B.PH[j][16 * g4 + 8]) = cat(l, l);
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
@@ -530,7 +544,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
 }
 
 // ---------------------------------------------------------------------------
-// consumer wave: the S-dependent chain of one chunk; returns O (D layout)
+// consumer wave: the S-dependent chain of one chunk; returns O transposed in
+// the D layout: lane (j, g4) holds O[token j][columns 4 g4 .. 4 g4 + 3]
 // ---------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16], int wave,
@@ -566,19 +581,21 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 const bf16x8 ql = cat(ld4b(&B.QL[j][kk]), ld4b(&B.QL[j][kk + 16]));
                 x = mma32(nk, sh, x);
                 x = mma32(nk, sl, x);
-                o = mma32(qh, sh, o);            // QE Sd: the lo x lo term
-                o = mma32(qh, sl, o);            // (2^-18) is dropped
-                o = mma32(ql, sh, o);
+                // O^T = Sd^T QE^T: the state is the A operand, so each lane
+                // ends with four consecutive output columns of one token
+                o = mma32(sh, qh, o);            // the lo x lo term
+                o = mma32(sl, qh, o);            // (2^-18) is dropped
+                o = mma32(sh, ql, o);
             }
         } else {
             // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
             bf16x4 hh, ll;
             split4(S[0], hh, ll);
             const bf16x4 nk = ld4b(&B.NK[j][4 * g4]);
-            const bf16x8 qq = cat(ld4b(&B.QH[j][4 * g4]), ld4b(&B.QL[j][4 * g4]));
+            const bf16x4 qh = ld4b(&B.QH[j][4 * g4]), ql = ld4b(&B.QL[j][4 * g4]);
             x = mma32(cat(nk, nk), cat(hh, ll), x);
-            o = mma32(qq, cat(hh, hh), o);                   // (Qh + Ql) Sh
-            o = mma32(qq, cat(ll, ll), o);                   // (Qh + Ql) Sl
+            o = mma32(cat(hh, ll), cat(qh, qh), o);          // (Sh + Sl) Qh
+            o = mma32(cat(hh, ll), cat(ql, ql), o);          // (Sh + Sl) Ql
         }
         // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
         bf16x8 xhh, xll, uhh, ull;
@@ -586,11 +603,14 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
         const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
         u = mma32(tt, xhh, zero);
         u = mma32(tt, xll, u);
-        split_hl(u, uhh, ull);
-        // O += P U
-        const bf16x8 pp = ld8b(&B.PH[j][8 * g4]);
-        o = mma32(pp, uhh, o);
-        o = mma32(pp, ull, o);
+        bf16x4 uh, ul;
+        split4(u, uh, ul);
+        uhh = cat(uh, uh);
+        ull = cat(ul, ul);
+        // O^T += U^T P^T: [Uh | Ul] against [Ph | Ph] and [Pl | Pl]
+        const bf16x8 uhl = cat(uh, ul);
+        o = mma32(uhl, ld8b(&B.PH[j][16 * g4]), o);
+        o = mma32(uhl, ld8b(&B.PH[j][16 * g4 + 8]), o);
         // S' = Sd + Kd^T U
 #pragma unroll
         for (int t = 0; t < C::DK / 16; ++t) {
@@ -606,14 +626,14 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             for (int i = 0; i < 4; ++i) {
                 const int kk = 16 * t + 4 * g4 + i;
                 x = mma4(B.NK[j][kk], S[t][i], x);
-                o = mma4(B.QH[j][kk], S[t][i], o);
+                o = mma4(S[t][i], B.QH[j][kk], o);           // O^T
             }
         }
         u = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) u = mma4(B.TH[j][4 * g4 + i], x[i], u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o = mma4(B.PH[j][4 * g4 + i], u[i], o);
+        for (int i = 0; i < 4; ++i) o = mma4(u[i], B.PH[j][4 * g4 + i], o);
 #pragma unroll
         for (int t = 0; t < C::DK / 16; ++t) {
 #pragma unroll
@@ -748,17 +768,13 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         // O of chunk c is written at the start of iteration c + 1, so the
         // stores overlap the next chain instead of delaying this one.
         const int rowo = H * DV;
-        int ooff[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ooff[i] = (int)(((4 * g4 + i) * rowo + h * DV + col_base + 16 * wave + j) *
-                            sizeof(TO));
+        // lane (j, g4) holds O[token j][columns 16 wave + 4 g4 .. + 3]
+        const int ooff = (j * rowo + h * DV + col_base + 16 * wave + 4 * g4) * (int)sizeof(TO);
         f32x4 ov = {0.f, 0.f, 0.f, 0.f};
         auto store_o = [&](int cc) {
             const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
                                         (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int)sizeof(TO));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bstore(ro, ooff[i], (TO)ov[i]);
+            bstore4(ro, ooff, ov, TO{});
         };
         __syncthreads();
         __syncthreads();
