@@ -184,7 +184,9 @@ struct Cfg {
     // P rows (bf16): each group of four tokens as [4 hi | 4 hi | 4 lo | 4 lo]
     // (B operands of the transposed output product), 144-byte stride
     static constexpr int LDQ = BF ? 72 : 20;
-    static constexpr int LDV = BV + (BF ? 8 : 4);
+    // v block stored transposed, [column][token]: a consumer lane reads its
+    // four tokens of one column with one vector read
+    static constexpr int LVT = BF ? 24 : 20;
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
     static constexpr int CW = DK / NW;
     static constexpr int CPW = CW / 2;
@@ -207,7 +209,7 @@ struct alignas(16) Buf {
     OT KH[C::DK][C::LDT];                // Kd^T                 [channel][token]
     OT TH[16][C::LDP];                   // T                    [token r][token i]
     OT PH[16][C::LDQ];                   // P
-    OT V[16][C::LDV];                    // value block
+    OT VT[C::BV][C::LVT];                // value block, transposed  [column][token]
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
 };
@@ -380,7 +382,14 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
     {
         // v is stored in its input type: the raw bits are copied
         const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-        *reinterpret_cast<typename Raw<C>::P4 *>(&B.V[row][4 * c4]) = r.v;
+        if constexpr (C::BF) {
+            const bf16x4 x = __builtin_bit_cast(bf16x4, r.v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) B.VT[4 * c4 + e][row] = x[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) B.VT[4 * c4 + e][row] = __uint_as_float(r.v[e]);
+        }
     }
     if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
 }
@@ -556,13 +565,21 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 x, u, o = zero;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (float)B.V[4 * g4 + i][vc];
+    for (int i = 0; i < 4; ++i) x[i] = (float)B.VT[vc][4 * g4 + i];
     // Sd = Diag(e^{Gc_16}) S
 #pragma unroll
     for (int t = 0; t < C::DK / 16; ++t)
         S[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 
     if constexpr (C::BF) {
+        // T and P of the chunk are final when the chunk starts: read first
+        const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
+        const bf16x8 ph2 = ld8b(&B.PH[j][16 * g4]), pl2 = ld8b(&B.PH[j][16 * g4 + 8]);
+        bf16x8 kd[C::DK / 16];
+        auto load_kd = [&]() {
+#pragma unroll
+            for (int t = 0; t < C::DK / 16; ++t) kd[t] = ld8b(&B.KH[16 * t + j][8 * g4]);
+        };
         // Sd as a bf16 hi/lo pair of B operands.  For d_k >= 32 the K slot
         // (g4, i) of step s is channel 32 s + 4 g4 + i (i < 4, tile 2s) or
         // 32 s + 16 + 4 g4 + (i - 4) (tile 2s + 1); A operands are read with
@@ -571,6 +588,14 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             constexpr int NS = C::DK / 32;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
+                if (s == NS - 1) {
+                    // the state-update operands are issued here (the earlier
+                    // steps' operand registers are free again), so they
+                    // arrive while the last step and the U chain run; the
+                    // scheduling barrier keeps the compiler from sinking them
+                    load_kd();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 bf16x4 h0, l0, h1, l1;
                 split4(S[2 * s], h0, l0);
                 split4(S[2 * s + 1], h1, l1);
@@ -589,6 +614,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             }
         } else {
             // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
+            load_kd();
             bf16x4 hh, ll;
             split4(S[0], hh, ll);
             const bf16x4 nk = ld4b(&B.NK[j][4 * g4]);
@@ -600,7 +626,6 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
         // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
         bf16x8 xhh, xll, uhh, ull;
         split_hl(x, xhh, xll);
-        const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
         u = mma32(tt, xhh, zero);
         u = mma32(tt, xll, u);
         bf16x4 uh, ul;
@@ -609,14 +634,13 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
         ull = cat(ul, ul);
         // O^T += U^T P^T: [Uh | Ul] against [Ph | Ph] and [Pl | Pl]
         const bf16x8 uhl = cat(uh, ul);
-        o = mma32(uhl, ld8b(&B.PH[j][16 * g4]), o);
-        o = mma32(uhl, ld8b(&B.PH[j][16 * g4 + 8]), o);
+        o = mma32(uhl, ph2, o);
+        o = mma32(uhl, pl2, o);
         // S' = Sd + Kd^T U
 #pragma unroll
         for (int t = 0; t < C::DK / 16; ++t) {
-            const bf16x8 kd = ld8b(&B.KH[16 * t + j][8 * g4]);
-            S[t] = mma32(kd, uhh, S[t]);
-            S[t] = mma32(kd, ull, S[t]);
+            S[t] = mma32(kd[t], uhh, S[t]);
+            S[t] = mma32(kd[t], ull, S[t]);
         }
     } else {
         // fp32: K index of slot (g4) in step (t, i) is 16 t + 4 g4 + i
