@@ -76,25 +76,37 @@ __device__ __forceinline__ bf16x8 ld8b(const bf16 *p) { return *reinterpret_cast
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// Two floats as packed bf16 words h = RNE(x) and l = RNE(x - h): one packed
-// conversion each, with h brought back to fp32 by a shift and a mask.
-__device__ __forceinline__ void split2(float a, float b, uint32_t &h, uint32_t &l)
-{
-    h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
-    l = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
-}
+// two floats as one packed bf16 word, round to nearest even
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-__device__ __forceinline__ void split4(f32x4 x, bf16x4 &h, bf16x4 &l)
+// Exact bf16 residuals on the matrix core, lane by lane.  In the 16x16x32
+// bf16 product, lane (n, g) = (lane % 16, lane / 16) holds D[4 g + i][n] of
+// the accumulator and B[8 g + i][n] of the B operand, and the A operand row
+// m has its K slots 8 (m / 4) + (m % 4) held by lane (m, m / 4).  With A the
+// negative identity placed on those slots (NegEye below), D = C - B' where
+// B' are the four values the same lane put in its own slots 0..3: any four
+// floats x of a lane and their bf16 roundings h give x - h in one product.
+// The product -h is exact and x - h is representable in fp32 when h is the
+// round-to-nearest of x, so the sum is exact; this costs one MFMA in place of
+// the shift, mask and two subtractions per pair on the vector ALU.
+struct NegEye {
+    bf16x8 a;
+};
+__device__ __forceinline__ NegEye neg_eye(int lane)
 {
-    uint32_t h0, l0, h1, l1;
-    split2(x[0], x[1], h0, l0);
-    split2(x[2], x[3], h1, l1);
-    h = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
-    l = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
+    const int m = lane & 15, kg = lane >> 4;
+    NegEye e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e.a[i] = (i < 4 && m == 4 * kg + i) ? (bf16)-1.0f : (bf16)0.0f;
+    return e;
+}
+__device__ __forceinline__ void split4(f32x4 x, const NegEye &ne, bf16x4 &h, bf16x4 &l)
+{
+    h = __builtin_bit_cast(bf16x4, u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])});
+    const f32x4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ne.a, cat(h, bf16x4{}), x, 0, 0, 0);
+    l = __builtin_bit_cast(bf16x4, u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])});
 }
 __device__ __forceinline__ int64_t uniform64(int64_t x)
 {
@@ -108,10 +120,10 @@ __device__ __forceinline__ float bcast(float x, int lane)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 // hi/lo split of a D-layout tile packed as 32-deep B operands [hi; hi], [lo; lo]
-__device__ __forceinline__ void split_hl(f32x4 x, bf16x8 &hh, bf16x8 &ll)
+__device__ __forceinline__ void split_hl(f32x4 x, const NegEye &ne, bf16x8 &hh, bf16x8 &ll)
 {
     bf16x4 h, l;
-    split4(x, h, l);
+    split4(x, ne, h, l);
     hh = cat(h, h);
     ll = cat(l, l);
 }
@@ -174,18 +186,26 @@ struct Cfg {
     static constexpr int BV = 16 * NW;             // state columns per workgroup
     static constexpr int NT = (2 * NW + 1) * WAVE; // consumers, builders, helper
     static constexpr int NC = NW * WAVE;           // consumer (= builder) threads
-    static constexpr int LDK = DK + (BF ? 8 : 4);  // row stride of [16][DK] arrays
+    // LDS strides.  gfx950 serves a 16-byte LDS access in four groups of 16
+    // lanes (the quads of equal bit parity inside each half wave) over 64
+    // four-byte banks.  A read where lane (j, g) = (lane % 16, lane / 16)
+    // takes 16 bytes at row j, byte 16 g of its row is then free of bank
+    // conflicts exactly when the row stride is an odd multiple of 32 bytes;
+    // every operand row below that is read this way has such a stride.
+    //
+    // [16][DK] operand rows (bf16, d_k >= 32): inside every block of 32
+    // channels the channels are stored in the order 0-3, 16-19, 4-7, 20-23,
+    // 8-11, 24-27, 12-15, 28-31 (kpos below), so the eight K slots of one
+    // consumer lane in a 32-deep product (channels 4 g + i and 16 + 4 g + i)
+    // are one 16-byte read
+    static constexpr int LDK = !BF ? DK + 4 : DK < 32 ? DK + 8 : ((DK / 8) % 4 == 2 ? DK : DK + 16);
     // Kd^T, T and P rows: bf16 rows hold each group of four tokens as
-    // [4 hi | 4 lo], so one 16-byte read is an MFMA A operand; the 80-byte
-    // row stride keeps those reads and the builder's writes at the minimum
-    // LDS bank-conflict degree
-    static constexpr int LDT = BF ? 40 : 20;       // row stride of Kd^T [DK][16]
-    static constexpr int LDP = BF ? 40 : 20;       // row stride of T [16][16]
-    // P rows (bf16): each group of four tokens as [4 hi | 4 hi | 4 lo | 4 lo]
-    // (B operands of the transposed output product), 144-byte stride
-    static constexpr int LDQ = BF ? 72 : 20;
+    // [4 hi | 4 lo] (Kd^T, T), [4 hi | 4 hi] (P hi) or [4 lo | 4 lo] (P lo),
+    // so one 16-byte read is an MFMA operand; 96-byte rows
+    static constexpr int LDT = BF ? 48 : 20;       // row stride of Kd^T [DK][16]
+    static constexpr int LDP = BF ? 48 : 20;       // row stride of T and P [16][16]
     // v block stored transposed, [column][token]: a consumer lane reads its
-    // four tokens of one column with one vector read
+    // four tokens of one column with one 8-byte read (48-byte rows)
     static constexpr int LVT = BF ? 24 : 20;
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
     static constexpr int CW = DK / NW;
@@ -193,6 +213,7 @@ struct Cfg {
     static constexpr int NG = WAVE / CPW;
     static constexpr int TPG = 16 / NG;
     static constexpr int LO = BF ? 1 : 0;          // hi/lo split present
+    static constexpr int NR = BF ? 3 : 2;          // builder raw-input register sets
     static_assert(CW >= 16 && CW <= 128, "builder mapping needs 16 <= d_k/NW <= 128");
     static_assert(NG * TPG == 16, "token groups");
     static_assert(NBUF >= 3, "one barrier per chunk needs three ring slots");
@@ -208,11 +229,24 @@ struct alignas(16) Buf {
     OT DL[C::LO ? 16 : 1][C::LDK];       // Kd lo
     OT KH[C::DK][C::LDT];                // Kd^T                 [channel][token]
     OT TH[16][C::LDP];                   // T                    [token r][token i]
-    OT PH[16][C::LDQ];                   // P
+    OT PH[16][C::LDP];                   // P (hi)
+    OT PL[C::LO ? 16 : 1][C::LDP];       // P lo
     OT VT[C::BV][C::LVT];                // value block, transposed  [column][token]
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
 };
+
+// stored position of key channel c in a [16][DK] operand row (see LDK)
+template <class C>
+__device__ __forceinline__ int kpos(int c)
+{
+    if constexpr (C::BF && C::DK >= 32) {
+        const int q = (c >> 2) & 7;
+        return (c & ~31) | ((q & 3) << 3) | ((q >> 2) << 2) | (c & 3);
+    } else {
+        return c;
+    }
+}
 
 template <class C>
 struct alignas(16) Smem {
@@ -224,10 +258,10 @@ struct alignas(16) Smem {
 template <class C>
 struct Raw {
     typedef typename std::conditional<C::BF, uint32_t, u32x2>::type P2;   // 2 q/k elements
-    typedef typename std::conditional<C::BF, u32x2, u32x4>::type P4;      // 4 v elements
     P2 q[C::TPG], k[C::TPG];
     u32x2 g[C::TPG];
-    P4 v;
+    // 4 tokens of one v column (bf16: packed pairs, fp32: one per word)
+    typename std::conditional<C::BF, u32x2, u32x4>::type v;
     uint32_t beta;
 };
 
@@ -271,10 +305,21 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
         }
         r.g[t] = bload64(rg, e * 4);
     }
-    const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-    const int ev = row * rowv + h * DV + col_base + 4 * c4;
-    if constexpr (C::BF) r.v = bload64(rv, ev * ES);
-    else r.v = bload128(rv, ev * ES);
+    // v: thread (column c, token quad tq) loads tokens 4 tq .. 4 tq + 3 of
+    // column c (a wave's loads of one token are consecutive columns)
+    const int c = tid % C::BV, tq = tid / C::BV;
+    const int ev = 4 * tq * rowv + h * DV + col_base + c;
+    if constexpr (C::BF) {
+        // 16-bit loads straight into the halves of two packed registers
+        typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+        u16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, (ev + i * rowv) * ES, 0, 0);
+        r.v = __builtin_bit_cast(u32x2, x);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.v[i] = bload32(rv, (ev + i * rowv) * ES);
+    }
     r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
 }
 
@@ -290,6 +335,8 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
     const int tok0 = tg * TPG;
+    const int kc = kpos<C>(ch);           // stored position of the pair (ch, ch + 1)
+    const NegEye ne = neg_eye(lane);
 
     // cumulative log2-decay over this lane's tokens, then across token groups
     float G0[TPG], G1[TPG];
@@ -325,20 +372,22 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         const float qe0 = qa * e0, qe1 = qb * e1;
         const float kd0 = ka * f0, kd1 = kb * f1;
         if constexpr (C::BF) {
-            uint32_t qh, ql, dh, dl;
-            split2(qe0, qe1, qh, ql);
-            split2(kd0, kd1, dh, dl);
-            *reinterpret_cast<uint32_t *>(&B.NK[tok][ch]) = pack2(-ka * e0, -kb * e1);
-            *reinterpret_cast<uint32_t *>(&B.QH[tok][ch]) = qh;
-            *reinterpret_cast<uint32_t *>(&B.QL[tok][ch]) = ql;
-            *reinterpret_cast<uint32_t *>(&B.DH[tok][ch]) = dh;
-            *reinterpret_cast<uint32_t *>(&B.DL[tok][ch]) = dl;
+            // QE and Kd of the channel pair as hi/lo bf16 pairs
+            bf16x4 hq, lq;
+            split4(f32x4{qe0, qe1, kd0, kd1}, ne, hq, lq);
+            const u32x2 hw = __builtin_bit_cast(u32x2, hq), lw = __builtin_bit_cast(u32x2, lq);
+            const uint32_t qh = hw[0], ql = lw[0], dh = hw[1], dl = lw[1];
+            *reinterpret_cast<uint32_t *>(&B.NK[tok][kc]) = pack2(-ka * e0, -kb * e1);
+            *reinterpret_cast<uint32_t *>(&B.QH[tok][kc]) = qh;
+            *reinterpret_cast<uint32_t *>(&B.QL[tok][kc]) = ql;
+            *reinterpret_cast<uint32_t *>(&B.DH[tok][kc]) = dh;
+            *reinterpret_cast<uint32_t *>(&B.DL[tok][kc]) = dl;
             const bf16x2 vh = __builtin_bit_cast(bf16x2, dh), vl = __builtin_bit_cast(bf16x2, dl);
             kdh0[t] = vh[0]; kdh1[t] = vh[1]; kdl0[t] = vl[0]; kdl1[t] = vl[1];
         } else {
-            *reinterpret_cast<OT2 *>(&B.NK[tok][ch]) = OT2{-ka * e0, -kb * e1};
-            *reinterpret_cast<OT2 *>(&B.QH[tok][ch]) = OT2{qe0, qe1};
-            *reinterpret_cast<OT2 *>(&B.DH[tok][ch]) = OT2{kd0, kd1};
+            *reinterpret_cast<OT2 *>(&B.NK[tok][kc]) = OT2{-ka * e0, -kb * e1};
+            *reinterpret_cast<OT2 *>(&B.QH[tok][kc]) = OT2{qe0, qe1};
+            *reinterpret_cast<OT2 *>(&B.DH[tok][kc]) = OT2{kd0, kd1};
             kdh0[t] = kd0; kdh1[t] = kd1;
         }
     }
@@ -380,16 +429,11 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         B.DEC[ch + 1] = fast_exp2(T1);
     }
     {
-        // v is stored in its input type: the raw bits are copied
-        const int row = tid / (C::BV / 4), c4 = tid % (C::BV / 4);
-        if constexpr (C::BF) {
-            const bf16x4 x = __builtin_bit_cast(bf16x4, r.v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) B.VT[4 * c4 + e][row] = x[e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) B.VT[4 * c4 + e][row] = __uint_as_float(r.v[e]);
-        }
+        // v is stored in its input type (the raw bits): four tokens of one
+        // column per thread, one 8- or 16-byte write
+        const int c = tid % C::BV, tq = tid / C::BV;
+        if constexpr (C::BF) *reinterpret_cast<u32x2 *>(&B.VT[c][4 * tq]) = r.v;
+        else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
     }
     if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
 }
@@ -456,6 +500,7 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     constexpr bool BF = C::BF;
     const int j = lane & 15, g4 = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const NegEye ne = neg_eye(lane);
     // With M = KE Kd^T (M[t][s] = KE_t . Kd_s):
     //   mt[e] (lane (j, g4)) = -M[j][4 g4 + e]       (D layout of -M^T)
     //   mc[e] (lane (j, g4)) = -M[4 g4 + e][j]       (D layout of -M)
@@ -463,7 +508,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     f32x4 mt = zero, mc = zero, pt = zero;
     if constexpr (BF) {
         if constexpr (C::DK >= 32) {
-            // K slot (g4, i) = channel 32 s + 8 g4 + i on both operands
+            // K slot (g4, i) = stored position 32 s + 8 g4 + i, the same
+            // channel on both operands
 #pragma unroll
             for (int s = 0; s < C::DK / 32; ++s) {
                 const int kk = 32 * s + 8 * g4;
@@ -506,9 +552,9 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
         for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e <= j) ? pt[e] : 0.f;
         if constexpr (BF) {
             bf16x4 h, l;
-            split4(f32x4{pv[0], pv[1], pv[2], pv[3]}, h, l);
-            *reinterpret_cast<bf16x8 *>(&B.PH[j][16 * g4]) = cat(h, h);
-            *reinterpret_cast<bf16x8 *>(&B.PH[j][16 * g4 + 8]) = cat(l, l);
+            split4(f32x4{pv[0], pv[1], pv[2], pv[3]}, ne, h, l);
+            *reinterpret_cast<bf16x8 *>(&B.PH[j][8 * g4]) = cat(h, h);
+            *reinterpret_cast<bf16x8 *>(&B.PL[j][8 * g4]) = cat(l, l);
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
@@ -545,7 +591,7 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     const f32x4 tv = tinv * b4;
     if constexpr (BF) {
         bf16x4 h, l;
-        split4(tv, h, l);
+        split4(tv, ne, h, l);
         *reinterpret_cast<bf16x8 *>(&B.TH[j][8 * g4]) = cat(h, l);
     } else {
         *reinterpret_cast<OT4 *>(&B.TH[j][4 * g4]) = OT4{tv[0], tv[1], tv[2], tv[3]};
@@ -563,6 +609,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     const int j = lane & 15, g4 = lane >> 4;
     const int vc = 16 * wave + j;           // column inside the block
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const NegEye ne = neg_eye(lane);
     f32x4 x, u, o = zero;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (float)B.VT[vc][4 * g4 + i];
@@ -574,7 +621,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     if constexpr (C::BF) {
         // T and P of the chunk are final when the chunk starts: read first
         const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
-        const bf16x8 ph2 = ld8b(&B.PH[j][16 * g4]), pl2 = ld8b(&B.PH[j][16 * g4 + 8]);
+        const bf16x8 ph2 = ld8b(&B.PH[j][8 * g4]), pl2 = ld8b(&B.PL[j][8 * g4]);
         bf16x8 kd[C::DK / 16];
         auto load_kd = [&]() {
 #pragma unroll
@@ -597,13 +644,14 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 bf16x4 h0, l0, h1, l1;
-                split4(S[2 * s], h0, l0);
-                split4(S[2 * s + 1], h1, l1);
+                split4(S[2 * s], ne, h0, l0);
+                split4(S[2 * s + 1], ne, h1, l1);
                 const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
-                const int kk = 32 * s + 4 * g4;
-                const bf16x8 nk = cat(ld4b(&B.NK[j][kk]), ld4b(&B.NK[j][kk + 16]));
-                const bf16x8 qh = cat(ld4b(&B.QH[j][kk]), ld4b(&B.QH[j][kk + 16]));
-                const bf16x8 ql = cat(ld4b(&B.QL[j][kk]), ld4b(&B.QL[j][kk + 16]));
+                // stored positions 32 s + 8 g4 .. + 7 hold exactly these channels
+                const int kk = 32 * s + 8 * g4;
+                const bf16x8 nk = ld8b(&B.NK[j][kk]);
+                const bf16x8 qh = ld8b(&B.QH[j][kk]);
+                const bf16x8 ql = ld8b(&B.QL[j][kk]);
                 x = mma32(nk, sh, x);
                 x = mma32(nk, sl, x);
                 // O^T = Sd^T QE^T: the state is the A operand, so each lane
@@ -616,7 +664,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             // d_k = 16: slot (g4, i) = channel 4 g4 + i%4 of Sd hi (i < 4) or lo
             load_kd();
             bf16x4 hh, ll;
-            split4(S[0], hh, ll);
+            split4(S[0], ne, hh, ll);
             const bf16x4 nk = ld4b(&B.NK[j][4 * g4]);
             const bf16x4 qh = ld4b(&B.QH[j][4 * g4]), ql = ld4b(&B.QL[j][4 * g4]);
             x = mma32(cat(nk, nk), cat(hh, ll), x);
@@ -625,11 +673,11 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
         }
         // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
         bf16x8 xhh, xll, uhh, ull;
-        split_hl(x, xhh, xll);
+        split_hl(x, ne, xhh, xll);
         u = mma32(tt, xhh, zero);
         u = mma32(tt, xll, u);
         bf16x4 uh, ul;
-        split4(u, uh, ul);
+        split4(u, ne, uh, ul);
         uhh = cat(uh, uh);
         ull = cat(ul, ul);
         // O^T += U^T P^T: [Uh | Ul] against [Ph | Ph] and [Pl | Pl]
@@ -741,36 +789,47 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     static_assert(NBUF == 3 && LAG == 2, "phase plan");
     if (is_build) {
         // Loads are issued unconditionally: buffer resources of chunks past
-        // the end are empty and read zeros.  Two register sets alternate
-        // (even chunks in ra, odd in rb), so a chunk's loads are issued two
-        // phases before its build.
-        Raw<C> ra, rb;
-        auto load = [&](Raw<C> &r, int cc) {
-            load_raw<C>(r, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
+        // the end are empty and read zeros.  NR register sets take chunks in
+        // turn (chunk cc in set cc % NR), so a chunk's loads are issued NR
+        // phases before its build: at one chunk per phase, the loads have
+        // NR phases to arrive, and NR sets of raw inputs are in flight.
+        constexpr int NR = C::NR;
+        Raw<C> r[NR];
+        auto load = [&](Raw<C> &x, int cc) {
+            load_raw<C>(x, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
                         col_base, bw, lane, btid);
         };
-        load(ra, 0);
-        load(rb, 1);
-        if (nch > 0) build<C>(sm.buf[0], ra, bw, lane, btid);
-        load(ra, 2);
-        if (nch > 1) build<C>(sm.buf[1], rb, bw, lane, btid);
-        load(rb, 3);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load(r[i], i);
+        if (nch > 0) build<C>(sm.buf[0], r[0], bw, lane, btid);
+        load(r[0], NR);
+        if (nch > 1) build<C>(sm.buf[1], r[1], bw, lane, btid);
+        load(r[1], NR + 1);
         __syncthreads();
         __syncthreads();
-        // (the odd last phase is peeled, so that every path back to the loop
-        // head has issued both register sets' loads in the same order and
-        // the compiler's counter waits let the newer set stay in flight)
+        // phase 2 + cc builds chunk cc + 2 from set (cc + 2) % NR and refills
+        // that set with chunk cc + 2 + NR.  The loop body is NR phases (c is
+        // a multiple of NR, so every set index is a constant) and the last
+        // nch % NR phases are peeled: every path back to the loop head has
+        // issued the sets' loads in the same order, so the compiler's counter
+        // waits keep the newer sets in flight.
         int c = 0;
 #pragma unroll 1
-        for (; c + 1 < nch; c += 2) {
-            if (c + 2 < nch) build<C>(slot((c + 2) % 3), ra, bw, lane, btid);
-            load(ra, c + 4);
-            __syncthreads();
-            if (c + 3 < nch) build<C>(slot((c + 3) % 3), rb, bw, lane, btid);
-            load(rb, c + 5);
-            __syncthreads();
+        for (; c + NR <= nch; c += NR) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid);
+                load(r[(i + 2) % NR], c + i + 2 + NR);
+                __syncthreads();
+            }
         }
-        if (c < nch) __syncthreads();           // phase of the last chunk (odd nch)
+#pragma unroll
+        for (int i = 0; i < NR - 1; ++i) {
+            if (c + i < nch) {
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid);
+                __syncthreads();
+            }
+        }
     } else if (!is_cons) {
         __syncthreads();
         if (nch > 0) helper<C>(sm.buf[0], lane);
