@@ -324,6 +324,46 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the NG token groups of a wave (group tg = lane /
+// CPW, one value per lane and group) and the total over all groups.  With 2
+// or 4 groups (halves or 16-lane rows of the wave) the exchanges are the
+// register swaps of v_permlane32_swap (lower with upper half) and
+// v_permlane16_swap (even with odd rows): no LDS round trip.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+template <int NG, int CPW>
+__device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &tot)
+{
+    if constexpr (NG == 1) {
+        incl = x;
+        tot = x;
+    } else if constexpr (NG == 2) {
+        // [0] = the lower half's value, [1] = the upper half's, in every lane
+        const auto h = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+        tot = bitsf(h[0]) + bitsf(h[1]);
+        incl = tg ? tot : x;
+    } else if constexpr (NG == 4) {
+        // [0] = the even row's value of this lane's row pair, [1] = the odd row's
+        const auto p = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+        const float pair = bitsf(p[0]) + bitsf(p[1]);
+        const float ip = (tg & 1) ? pair : x;
+        // pair totals of rows 0-1 ([0]) and rows 2-3 ([1])
+        const auto h = __builtin_amdgcn_permlane32_swap(fbits(pair), fbits(pair), false, false);
+        incl = (tg & 2) ? ip + bitsf(h[0]) : ip;
+        tot = bitsf(h[0]) + bitsf(h[1]);
+    } else {
+        incl = x;
+#pragma unroll
+        for (int off = 1; off < NG; off <<= 1) {
+            const float n = __shfl_up(incl, off * CPW, WAVE);
+            if (tg >= off) incl += n;
+        }
+        tot = __shfl(incl, (WAVE - CPW) + (__lane_id() % CPW), WAVE);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // build: raw registers -> end-referenced operands of one chunk in LDS
 // ---------------------------------------------------------------------------
 template <class C>
@@ -348,15 +388,10 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         G0[t] = s0;
         G1[t] = s1;
     }
-    float i0 = s0, i1 = s1;     // inclusive scan of group totals
-#pragma unroll
-    for (int off = 1; off < C::NG; off <<= 1) {
-        const float n0 = __shfl_up(i0, off * C::CPW, WAVE);
-        const float n1 = __shfl_up(i1, off * C::CPW, WAVE);
-        if (tg >= off) { i0 += n0; i1 += n1; }
-    }
-    const int last = cp + (C::NG - 1) * C::CPW;
-    const float T0 = __shfl(i0, last, WAVE), T1 = __shfl(i1, last, WAVE);  // Gc_16
+    // inclusive scan of the group totals, and the chunk total Gc_16
+    float i0, i1, T0, T1;
+    group_scan<C::NG, C::CPW>(s0, tg, i0, T0);
+    group_scan<C::NG, C::CPW>(s1, tg, i1, T1);
     // Gc_r - Gc_16 = (local prefix + exclusive offset) - total
     const float o0 = i0 - s0 - T0, o1 = i1 - s1 - T1;
 
