@@ -634,12 +634,43 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
 }
 
 // ---------------------------------------------------------------------------
+// Operands of a chunk that its builders have already finished (v block, the
+// decay of the first two state tiles, the first 32-deep step of -KE and QE).
+// The consumer reads them for chunk c + 1 before the barrier that ends chunk
+// c, so the next chain starts without waiting on LDS.  T and P, which the
+// helper writes during chunk c, are not among them.
+// ---------------------------------------------------------------------------
+template <class C>
+struct Ahead {
+    using OT = typename C::OT;
+    typedef OT OT4 __attribute__((ext_vector_type(4)));
+    OT4 v;
+    f32x4 dec[C::DK >= 32 ? 2 : 1];
+    bf16x8 nk, qh, ql;                   // bf16 with d_k >= 32 only
+};
+template <class C>
+__device__ __forceinline__ void read_ahead(const Buf<C> &B, Ahead<C> &a, int wave, int lane)
+{
+    typedef typename Ahead<C>::OT4 OT4;
+    const int j = lane & 15, g4 = lane >> 4;
+    a.v = *reinterpret_cast<const OT4 *>(&B.VT[16 * wave + j][4 * g4]);
+#pragma unroll
+    for (int t = 0; t < (C::DK >= 32 ? 2 : 1); ++t)
+        a.dec[t] = *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
+    if constexpr (C::BF && C::DK >= 32) {
+        a.nk = ld8b(&B.NK[j][8 * g4]);
+        a.qh = ld8b(&B.QH[j][8 * g4]);
+        a.ql = ld8b(&B.QL[j][8 * g4]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // consumer wave: the S-dependent chain of one chunk; returns O transposed in
 // the D layout: lane (j, g4) holds O[token j][columns 4 g4 .. 4 g4 + 3]
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16], int wave,
-                                         int lane)
+__device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16],
+                                         const Ahead<C> &ah, int wave, int lane)
 {
     const int j = lane & 15, g4 = lane >> 4;
     const int vc = 16 * wave + j;           // column inside the block
@@ -647,11 +678,12 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     const NegEye ne = neg_eye(lane);
     f32x4 x, u, o = zero;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (float)B.VT[vc][4 * g4 + i];
+    for (int i = 0; i < 4; ++i) x[i] = (float)ah.v[i];
     // Sd = Diag(e^{Gc_16}) S
 #pragma unroll
     for (int t = 0; t < C::DK / 16; ++t)
-        S[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
+        S[t] *= t < (C::DK >= 32 ? 2 : 1) ? ah.dec[t < 1 ? 0 : C::DK >= 32 ? 1 : 0]
+                                          : *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 
     if constexpr (C::BF) {
         // T and P of the chunk are final when the chunk starts: read first
@@ -684,9 +716,9 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
                 // stored positions 32 s + 8 g4 .. + 7 hold exactly these channels
                 const int kk = 32 * s + 8 * g4;
-                const bf16x8 nk = ld8b(&B.NK[j][kk]);
-                const bf16x8 qh = ld8b(&B.QH[j][kk]);
-                const bf16x8 ql = ld8b(&B.QL[j][kk]);
+                const bf16x8 nk = s == 0 ? ah.nk : ld8b(&B.NK[j][kk]);
+                const bf16x8 qh = s == 0 ? ah.qh : ld8b(&B.QH[j][kk]);
+                const bf16x8 ql = s == 0 ? ah.ql : ld8b(&B.QL[j][kk]);
                 x = mma32(nk, sh, x);
                 x = mma32(nk, sl, x);
                 // O^T = Sd^T QE^T: the state is the A operand, so each lane
@@ -896,10 +928,13 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         };
         __syncthreads();
         __syncthreads();
+        Ahead<C> ah;
+        read_ahead<C>(sm.buf[0], ah, wave, lane);
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             store_o(c - 1);
-            ov = consume<C>(slot(c % 3), S, wave, lane);
+            ov = consume<C>(slot(c % 3), S, ah, wave, lane);
+            read_ahead<C>(slot((c + 1) % 3), ah, wave, lane);
             __syncthreads();
         }
         if (nch > 0) store_o(nch - 1);
