@@ -27,6 +27,30 @@ __device__ __forceinline__ float u16_to_f(uint16_t b) {
 // 2^x on the hardware exponential unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Register exchanges across 16-lane rows and across half waves (gfx950).
+// v_permlane16_swap a, b trades the odd rows of a with the even rows of b;
+// v_permlane32_swap a, b trades the upper half of a with the lower half of
+// b.  Starting from a = b = x, afterwards a holds, in every lane, the value
+// of the even row of its row pair (upper: of the lower half) and b the value
+// of the odd row (upper half).  They are written as inline assembly: with the
+// same value in both operands, the compiler's handling of the swap builtins
+// was seen to merge the two results (a + b compiled as 2a).  The s_nop pairs
+// cover the two wait states between a vector write and the swap.
+__device__ __forceinline__ void row_pair(float x, float &even, float &odd)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    even = __builtin_bit_cast(float, a);
+    odd = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ void half_pair(float x, float &lower, float &upper)
+{
+    uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    lower = __builtin_bit_cast(float, a);
+    upper = __builtin_bit_cast(float, b);
+}
+
 // Element loads/stores that convert between the storage type and fp32.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -327,11 +327,9 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
 // Inclusive prefix sum over the NG token groups of a wave (group tg = lane /
 // CPW, one value per lane and group) and the total over all groups.  With 2
 // or 4 groups (halves or 16-lane rows of the wave) the exchanges are the
-// register swaps of v_permlane32_swap (lower with upper half) and
-// v_permlane16_swap (even with odd rows): no LDS round trip.
+// register swaps across half waves and row pairs (half_pair, row_pair): no
+// LDS round trip.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
 template <int NG, int CPW>
 __device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &tot)
 {
@@ -339,19 +337,19 @@ __device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &
         incl = x;
         tot = x;
     } else if constexpr (NG == 2) {
-        // [0] = the lower half's value, [1] = the upper half's, in every lane
-        const auto h = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
-        tot = bitsf(h[0]) + bitsf(h[1]);
+        float lo, hi;                    // the lower and the upper half's value
+        half_pair(x, lo, hi);
+        tot = lo + hi;
         incl = tg ? tot : x;
     } else if constexpr (NG == 4) {
-        // [0] = the even row's value of this lane's row pair, [1] = the odd row's
-        const auto p = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
-        const float pair = bitsf(p[0]) + bitsf(p[1]);
+        float ev, od;                    // the even and odd row of this row pair
+        row_pair(x, ev, od);
+        const float pair = ev + od;
         const float ip = (tg & 1) ? pair : x;
-        // pair totals of rows 0-1 ([0]) and rows 2-3 ([1])
-        const auto h = __builtin_amdgcn_permlane32_swap(fbits(pair), fbits(pair), false, false);
-        incl = (tg & 2) ? ip + bitsf(h[0]) : ip;
-        tot = bitsf(h[0]) + bitsf(h[1]);
+        float lo, hi;                    // pair totals of rows 0-1 and rows 2-3
+        half_pair(pair, lo, hi);
+        incl = (tg & 2) ? ip + lo : ip;
+        tot = lo + hi;
     } else {
         incl = x;
 #pragma unroll
