@@ -30,13 +30,13 @@
 //
 // Mapping.  One workgroup per (sequence, head, block of BV = 16 NW columns
 // of the state): the columns of S evolve independently, so the d_v split
-// needs no communication.  Three roles, 2 NW + 1 waves:
+// needs no communication.  Three roles, NW + NBW + 1 waves:
 //  * consumer wave w keeps S[:, 16w : 16w+16] of its block in registers in
 //    the 16x16 MFMA accumulator layout (lane l holds rows 4(l/16)+i, column
 //    l%16 of each 16x16 tile) and runs the S-dependent chain of chunk c;
-//  * builder wave w loads the raw inputs of a quarter of the key channels
-//    and builds the operands of chunk c+2 (cumulative sums, exponentials,
-//    bf16 hi/lo splits) into LDS;
+//  * builder wave w loads the raw inputs of 1/NBW of the key channels (and
+//    of the value block) and builds the operands of chunk c+2 (cumulative
+//    sums, exponentials, bf16 hi/lo splits) into LDS;
 //  * the helper wave forms A and P of chunk c+1 and the inverse of (I + A)
 //    as a product of four factors, all on the matrix cores.
 // A ring of three LDS operand slots needs one barrier per chunk.
@@ -182,10 +182,18 @@ struct Cfg {
     using OT = typename std::conditional<BF, bf16, float>::type;   // LDS operand type
     static constexpr int DK = DK_;
     static constexpr int NW = NW_;                 // consumer waves
+    // builder waves: up to four, each with at least 16 key channels; the
+    // count does not depend on the block width, so narrow blocks (used when
+    // there are too few chains to fill the device) keep the build rate
+    static constexpr int NBW = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
-    static constexpr int NT = (2 * NW + 1) * WAVE; // consumers, builders, helper
-    static constexpr int NC = NW * WAVE;           // consumer (= builder) threads
+    static constexpr int NT = (NW + NBW + 1) * WAVE;   // consumers, builders, helper
+    static constexpr int NC = NW * WAVE;           // consumer threads
+    static constexpr int NVT = 4 * BV;             // builder threads that move v (4 tokens each)
+    static_assert(NVT <= NBW * WAVE && NVT % WAVE == 0, "value block mapping");
+    // builder thread tid moves v
+    static __device__ __forceinline__ bool all_v(int tid) { return NVT == NBW * WAVE || tid < NVT; }
     // LDS strides.  gfx950 serves a 16-byte LDS access in four groups of 16
     // lanes (the quads of equal bit parity inside each half wave) over 64
     // four-byte banks.  A read where lane (j, g) = (lane % 16, lane / 16)
@@ -208,13 +216,13 @@ struct Cfg {
     // four tokens of one column with one 8-byte read (48-byte rows)
     static constexpr int LVT = BF ? 24 : 20;
     // builder: wave w owns CW key channels; lane = (channel pair, token group)
-    static constexpr int CW = DK / NW;
+    static constexpr int CW = DK / NBW;
     static constexpr int CPW = CW / 2;
     static constexpr int NG = WAVE / CPW;
     static constexpr int TPG = 16 / NG;
     static constexpr int LO = BF ? 1 : 0;          // hi/lo split present
     static constexpr int NR = BF ? 3 : 2;          // builder raw-input register sets
-    static_assert(CW >= 16 && CW <= 128, "builder mapping needs 16 <= d_k/NW <= 128");
+    static_assert(CW >= 16 && CW <= 128, "builder mapping needs 16 <= d_k/NBW <= 128");
     static_assert(NG * TPG == 16, "token groups");
     static_assert(NBUF >= 3, "one barrier per chunk needs three ring slots");
 };
@@ -305,8 +313,11 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
         }
         r.g[t] = bload64(rg, e * 4);
     }
-    // v: thread (column c, token quad tq) loads tokens 4 tq .. 4 tq + 3 of
-    // column c (a wave's loads of one token are consecutive columns)
+    r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
+    // v: thread (column c, token quad tq) < NVT loads tokens 4 tq .. 4 tq + 3
+    // of column c (a wave's loads of one token are consecutive columns); the
+    // condition is uniform over each wave and absent when all builders move v
+    if (!C::all_v(tid)) return;
     const int c = tid % C::BV, tq = tid / C::BV;
     const int ev = 4 * tq * rowv + h * DV + col_base + c;
     if constexpr (C::BF) {
@@ -320,7 +331,6 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
 #pragma unroll
         for (int i = 0; i < 4; ++i) r.v[i] = bload32(rv, (ev + i * rowv) * ES);
     }
-    r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -465,8 +475,10 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         // v is stored in its input type (the raw bits): four tokens of one
         // column per thread, one 8- or 16-byte write
         const int c = tid % C::BV, tq = tid / C::BV;
-        if constexpr (C::BF) *reinterpret_cast<u32x2 *>(&B.VT[c][4 * tq]) = r.v;
-        else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
+        if (C::all_v(tid)) {
+            if constexpr (C::BF) *reinterpret_cast<u32x2 *>(&B.VT[c][4 * tq]) = r.v;
+            else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
+        }
     }
     if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
 }
@@ -825,9 +837,9 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // roles: consumer waves 0 .. NW-1, builder waves NW .. 2NW-1, one helper
+    // roles: consumer waves 0 .. NW-1, builder waves NW .. NW+NBW-1, one helper
     const bool is_cons = wave < NW;
-    const bool is_build = !is_cons && wave < 2 * NW;
+    const bool is_build = !is_cons && wave < NW + C::NBW;
     const int bw = wave - NW, btid = tid - C::NC;     // builder wave / thread index
     const int j = lane & 15, g4 = lane >> 4;
 
@@ -964,11 +976,13 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains)
     return hipGetLastError();
 }
 
-// waves per workgroup: 16 columns per consumer wave, at most 4 consumers
+// waves per workgroup: 16 columns per consumer wave, at most 4 consumers and
+// no more than the builder waves (each builder thread moves at most one
+// four-token column piece of the value block)
 template <int DK, int DV>
 struct PickNW {
     static constexpr int byv = DV / 16 < 4 ? DV / 16 : 4;
-    static constexpr int bydk = DK / 16;                 // builder needs d_k/NW >= 16
+    static constexpr int bydk = DK / 16;
     static constexpr int value = byv < bydk ? byv : bydk;
 };
 
