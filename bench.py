@@ -101,7 +101,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the first ~100 launches run at lower clocks; the default warmup reaches
+    # the steady state before the timed region
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "long_prefill", "varlen", "varlen_1m"])
     ap.add_argument("--no-decode", action="store_true")

@@ -30,15 +30,16 @@
 //
 // Mapping.  One workgroup per (sequence, head, block of BV = 16 NW columns
 // of the state): the columns of S evolve independently, so the d_v split
-// needs no communication.  Three roles, NW + NBW + 1 waves:
+// needs no communication.  Three roles, NW + NBW + 2 waves:
 //  * consumer wave w keeps S[:, 16w : 16w+16] of its block in registers in
 //    the 16x16 MFMA accumulator layout (lane l holds rows 4(l/16)+i, column
 //    l%16 of each 16x16 tile) and runs the S-dependent chain of chunk c;
 //  * builder wave w loads the raw inputs of 1/NBW of the key channels (and
 //    of the value block) and builds the operands of chunk c+2 (cumulative
 //    sums, exponentials, bf16 hi/lo splits) into LDS;
-//  * the helper wave forms A and P of chunk c+1 and the inverse of (I + A)
-//    as a product of four factors, all on the matrix cores.
+//  * two helper waves, on different SIMDs, form A of chunk c+1 and the
+//    inverse of (I + A) as a product of four factors, and P of chunk c+1,
+//    all on the matrix cores.
 // A ring of three LDS operand slots needs one barrier per chunk.
 //
 // Precision.  bf16 inputs: matrix-core operands are bf16 with fp32
@@ -188,7 +189,7 @@ struct Cfg {
     static constexpr int NBW = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
-    static constexpr int NT = (NW + NBW + 1) * WAVE;   // consumers, builders, helper
+    static constexpr int NT = (NW + NBW + 2) * WAVE;   // consumers, builders, 2 helpers
     static constexpr int NC = NW * WAVE;           // consumer threads
     static constexpr int NVT = 4 * BV;             // builder threads that move v (4 tokens each)
     static_assert(NVT <= NBW * WAVE && NVT % WAVE == 0, "value block mapping");
@@ -525,7 +526,7 @@ __device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
 }
 
 // ---------------------------------------------------------------------------
-// helper wave: A, P and T = (I + A)^{-1} Diag(beta) for one chunk
+// helper waves: A and T = (I + A)^{-1} Diag(beta) (PART 0), P (PART 1)
 //
 // A is strictly lower triangular, so A^16 = 0 and
 //   (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
@@ -537,7 +538,7 @@ __device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
 // emulation against the oracle: no change in the error of o or S_T); T is
 // then written as a hi/lo pair.
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, int PART>
 __device__ __forceinline__ void helper(Buf<C> &B, int lane)
 {
     using OT = typename C::OT;
@@ -558,14 +559,18 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
 #pragma unroll
             for (int s = 0; s < C::DK / 32; ++s) {
                 const int kk = 32 * s + 8 * g4;
-                const bf16x8 nk = ld8b(&B.NK[j][kk]);
-                const bf16x8 qh = ld8b(&B.QH[j][kk]), ql = ld8b(&B.QL[j][kk]);
-                const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
-                mt = mma32(dh, nk, mt);
-                mc = mma32(nk, dh, mc);
-                pt = mma32(dh, qh, pt);
-                pt = mma32(dl, qh, pt);
-                pt = mma32(dh, ql, pt);
+                const bf16x8 dh = ld8b(&B.DH[j][kk]);
+                if constexpr (PART == 0) {
+                    const bf16x8 nk = ld8b(&B.NK[j][kk]);
+                    mt = mma32(dh, nk, mt);
+                    mc = mma32(nk, dh, mc);
+                } else {
+                    const bf16x8 qh = ld8b(&B.QH[j][kk]), ql = ld8b(&B.QL[j][kk]);
+                    const bf16x8 dl = ld8b(&B.DL[j][kk]);
+                    pt = mma32(dh, qh, pt);
+                    pt = mma32(dl, qh, pt);
+                    pt = mma32(dh, ql, pt);
+                }
             }
         } else {
             // d_k = 16: K slot (g4, i) = channel 4 g4 + i%4 of the hi (i < 4)
@@ -576,22 +581,28 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
             const bf16x4 dh = ld4b(&B.DH[j][kk]);
             const bf16x8 dd = cat(dh, ld4b(&B.DL[j][kk]));
             const bf16x4 z = {};
-            mt = mma32(cat(dh, z), cat(nk, z), mt);
-            mc = mma32(cat(nk, z), cat(dh, z), mc);
-            pt = mma32(dd, cat(qh, qh), pt);    // (dh + dl) qh
-            pt = mma32(dd, cat(ql, ql), pt);    // (dh + dl) ql
+            if constexpr (PART == 0) {
+                mt = mma32(cat(dh, z), cat(nk, z), mt);
+                mc = mma32(cat(nk, z), cat(dh, z), mc);
+            } else {
+                pt = mma32(dd, cat(qh, qh), pt);    // (dh + dl) qh
+                pt = mma32(dd, cat(ql, ql), pt);    // (dh + dl) ql
+            }
         }
     } else {
 #pragma unroll 8
         for (int s = 0; s < C::DK / 4; ++s) {
             const int kk = 4 * s + g4;
-            mt = mma4(B.DH[j][kk], B.NK[j][kk], mt);
-            mc = mma4(B.NK[j][kk], B.DH[j][kk], mc);
-            pt = mma4(B.DH[j][kk], B.QH[j][kk], pt);
+            if constexpr (PART == 0) {
+                mt = mma4(B.DH[j][kk], B.NK[j][kk], mt);
+                mc = mma4(B.NK[j][kk], B.DH[j][kk], mc);
+            } else {
+                pt = mma4(B.DH[j][kk], B.QH[j][kk], pt);
+            }
         }
     }
     // P row j (lower triangle including the diagonal)
-    {
+    if constexpr (PART == 1) {
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = (4 * g4 + e <= j) ? pt[e] : 0.f;
@@ -603,6 +614,7 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
         } else {
             *reinterpret_cast<OT4 *>(&B.PH[j][4 * g4]) = OT4{pv[0], pv[1], pv[2], pv[3]};
         }
+        return;
     }
     // A[t][s] = beta_t M[t][s] (s < t), in D layout (a) and transposed (at)
     const float bj = B.BETA[j];
@@ -837,7 +849,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // roles: consumer waves 0 .. NW-1, builder waves NW .. NW+NBW-1, one helper
+    // roles: consumer waves 0 .. NW-1, builder waves NW .. NW+NBW-1, two helpers
     const bool is_cons = wave < NW;
     const bool is_build = !is_cons && wave < NW + C::NBW;
     const int bw = wave - NW, btid = tid - C::NC;     // builder wave / thread index
@@ -855,14 +867,15 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     // Pipeline over chunks with a ring of NBUF = 3 operand slots, in phases
     // separated by barriers (every role passes the same nch + 2 barriers):
     //   phase 0       builders build chunks 0 and 1
-    //   phase 1       helper forms A, P, T of chunk 0
-    //   phase 2 + c   builders build chunk c + 2 (slot (c + 2) % 3), helper
-    //                 forms A, P, T of chunk c + 1 (slot (c + 1) % 3),
+    //   phase 1       helpers form A, P, T of chunk 0
+    //   phase 2 + c   builders build chunk c + 2 (slot (c + 2) % 3), helpers
+    //                 form A, P, T of chunk c + 1 (slot (c + 1) % 3),
     //                 consumers store O of chunk c - 1 and run the S chain
     //                 of chunk c (slot c % 3)
     // Each SIMD holds one consumer and one builder wave, so the builder's
-    // VALU work fills the consumer's matrix-core and LDS waits.  Every role
-    // runs its own loop; the role is wave-uniform.
+    // VALU work fills the consumer's matrix-core and LDS waits; the two
+    // helper waves sit on SIMDs 0 and 1.  Every role runs its own loop; the
+    // role is wave-uniform.
     static_assert(NBUF == 3 && LAG == 2, "phase plan");
     if (is_build) {
         // Loads are issued unconditionally: buffer resources of chunks past
@@ -908,12 +921,17 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
             }
         }
     } else if (!is_cons) {
+        // two helper waves on different SIMDs: A and T, and P
+        auto help = [&](Buf<C> &B) {
+            if (wave == NW + C::NBW) helper<C, 0>(B, lane);
+            else helper<C, 1>(B, lane);
+        };
         __syncthreads();
-        if (nch > 0) helper<C>(sm.buf[0], lane);
+        if (nch > 0) help(sm.buf[0]);
         __syncthreads();
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
-            if (c + 1 < nch) helper<C>(slot((c + 1) % 3), lane);
+            if (c + 1 < nch) help(slot((c + 1) % 3));
             __syncthreads();
         }
     } else {
