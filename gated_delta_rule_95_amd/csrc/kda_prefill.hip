@@ -91,16 +91,22 @@ __device__ __forceinline__ uint32_t pack2(float a, float b)
 // floats x of a lane and their bf16 roundings h give x - h in one product.
 // The product -h is exact and x - h is representable in fp32 when h is the
 // round-to-nearest of x, so the sum is exact; this costs one MFMA in place of
-// the shift, mask and two subtractions per pair on the vector ALU.
+// the shift, mask and two subtractions per pair on the vector ALU.  The same
+// identity placed on the slots 4..7 (b below) takes the residual of the four
+// values in the lane's upper slots, so two tiles whose roundings share one
+// 8-slot operand [h0 | h1] need no zero padding and no copies.
 struct NegEye {
-    bf16x8 a;
+    bf16x8 a, b;
 };
 __device__ __forceinline__ NegEye neg_eye(int lane)
 {
     const int m = lane & 15, kg = lane >> 4;
     NegEye e;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e.a[i] = (i < 4 && m == 4 * kg + i) ? (bf16)-1.0f : (bf16)0.0f;
+    for (int i = 0; i < 8; ++i) {
+        e.a[i] = (i < 4 && m == 4 * kg + i) ? (bf16)-1.0f : (bf16)0.0f;
+        e.b[i] = (i >= 4 && m == 4 * kg + i - 4) ? (bf16)-1.0f : (bf16)0.0f;
+    }
     return e;
 }
 __device__ __forceinline__ void split4(f32x4 x, const NegEye &ne, bf16x4 &h, bf16x4 &l)
@@ -108,6 +114,17 @@ __device__ __forceinline__ void split4(f32x4 x, const NegEye &ne, bf16x4 &h, bf1
     h = __builtin_bit_cast(bf16x4, u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])});
     const f32x4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ne.a, cat(h, bf16x4{}), x, 0, 0, 0);
     l = __builtin_bit_cast(bf16x4, u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])});
+}
+// hi/lo split of two D-layout tiles into the 8-slot operands [h0 | h1] and
+// [l0 | l1]
+__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, const NegEye &ne, bf16x8 &h, bf16x8 &l)
+{
+    h = __builtin_bit_cast(bf16x8, u32x4{pack2(x0[0], x0[1]), pack2(x0[2], x0[3]),
+                                         pack2(x1[0], x1[1]), pack2(x1[2], x1[3])});
+    const f32x4 r0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ne.a, h, x0, 0, 0, 0);
+    const f32x4 r1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ne.b, h, x1, 0, 0, 0);
+    l = __builtin_bit_cast(bf16x8, u32x4{pack2(r0[0], r0[1]), pack2(r0[2], r0[3]),
+                                         pack2(r1[0], r1[1]), pack2(r1[2], r1[3])});
 }
 __device__ __forceinline__ int64_t uniform64(int64_t x)
 {
@@ -119,14 +136,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t x)
 __device__ __forceinline__ float bcast(float x, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
-// hi/lo split of a D-layout tile packed as 32-deep B operands [hi; hi], [lo; lo]
-__device__ __forceinline__ void split_hl(f32x4 x, const NegEye &ne, bf16x8 &hh, bf16x8 &ll)
-{
-    bf16x4 h, l;
-    split4(x, ne, h, l);
-    hh = cat(h, h);
-    ll = cat(l, l);
 }
 
 // Raw buffer resources: an access at a byte offset >= num_records reads 0
@@ -209,7 +218,8 @@ struct Cfg {
     // are one 16-byte read
     static constexpr int LDK = !BF ? DK + 4 : DK < 32 ? DK + 8 : ((DK / 8) % 4 == 2 ? DK : DK + 16);
     // Kd^T, T and P rows: bf16 rows hold each group of four tokens as
-    // [4 hi | 4 lo] (Kd^T, T), [4 hi | 4 hi] (P hi) or [4 lo | 4 lo] (P lo),
+    // [4 hi | 4 lo] (Kd^T), [4 hi | 4 hi] (T hi, P hi) or [4 lo | 4 lo] (T lo,
+    // P lo),
     // so one 16-byte read is an MFMA operand; 96-byte rows
     static constexpr int LDT = BF ? 48 : 20;       // row stride of Kd^T [DK][16]
     static constexpr int LDP = BF ? 48 : 20;       // row stride of T and P [16][16]
@@ -237,7 +247,8 @@ struct alignas(16) Buf {
     OT DH[16][C::LDK];                   // Kd hi                [token][channel]
     OT DL[C::LO ? 16 : 1][C::LDK];       // Kd lo
     OT KH[C::DK][C::LDT];                // Kd^T                 [channel][token]
-    OT TH[16][C::LDP];                   // T                    [token r][token i]
+    OT TH[16][C::LDP];                   // T (hi)               [token r][token i]
+    OT TL[C::LO ? 16 : 1][C::LDP];       // T lo
     OT PH[16][C::LDP];                   // P (hi)
     OT PL[C::LO ? 16 : 1][C::LDP];       // P lo
     OT VT[C::BV][C::LVT];                // value block, transposed  [column][token]
@@ -405,6 +416,7 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
     const float o0 = i0 - s0 - T0, o1 = i1 - s1 - T1;
 
     OT kdh0[TPG], kdh1[TPG], kdl0[TPG], kdl1[TPG];
+    f32x4 qk[TPG];                        // QE and Kd of the channel pair, per token
 #pragma unroll
     for (int t = 0; t < TPG; ++t) {
         const int tok = tok0 + t;
@@ -413,26 +425,37 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         const float f0 = fast_exp2(-d0), f1 = fast_exp2(-d1);         // 1 / E
         const float ka = elem<C>(r.k[t], 0), kb = elem<C>(r.k[t], 1);
         const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
-        const float qe0 = qa * e0, qe1 = qb * e1;
-        const float kd0 = ka * f0, kd1 = kb * f1;
+        qk[t] = f32x4{qa * e0, qb * e1, ka * f0, kb * f1};
         if constexpr (C::BF) {
-            // QE and Kd of the channel pair as hi/lo bf16 pairs
-            bf16x4 hq, lq;
-            split4(f32x4{qe0, qe1, kd0, kd1}, ne, hq, lq);
-            const u32x2 hw = __builtin_bit_cast(u32x2, hq), lw = __builtin_bit_cast(u32x2, lq);
-            const uint32_t qh = hw[0], ql = lw[0], dh = hw[1], dl = lw[1];
             *reinterpret_cast<uint32_t *>(&B.NK[tok][kc]) = pack2(-ka * e0, -kb * e1);
-            *reinterpret_cast<uint32_t *>(&B.QH[tok][kc]) = qh;
-            *reinterpret_cast<uint32_t *>(&B.QL[tok][kc]) = ql;
-            *reinterpret_cast<uint32_t *>(&B.DH[tok][kc]) = dh;
-            *reinterpret_cast<uint32_t *>(&B.DL[tok][kc]) = dl;
-            const bf16x2 vh = __builtin_bit_cast(bf16x2, dh), vl = __builtin_bit_cast(bf16x2, dl);
-            kdh0[t] = vh[0]; kdh1[t] = vh[1]; kdl0[t] = vl[0]; kdl1[t] = vl[1];
         } else {
             *reinterpret_cast<OT2 *>(&B.NK[tok][kc]) = OT2{-ka * e0, -kb * e1};
-            *reinterpret_cast<OT2 *>(&B.QH[tok][kc]) = OT2{qe0, qe1};
-            *reinterpret_cast<OT2 *>(&B.DH[tok][kc]) = OT2{kd0, kd1};
-            kdh0[t] = kd0; kdh1[t] = kd1;
+            *reinterpret_cast<OT2 *>(&B.QH[tok][kc]) = OT2{qk[t][0], qk[t][1]};
+            *reinterpret_cast<OT2 *>(&B.DH[tok][kc]) = OT2{qk[t][2], qk[t][3]};
+            kdh0[t] = qk[t][2]; kdh1[t] = qk[t][3];
+        }
+    }
+    if constexpr (C::BF) {
+        // QE and Kd of the channel pair as hi/lo bf16 pairs, two tokens per
+        // split (words: QE hi, Kd hi of token t, then of token t + 1)
+        static_assert(TPG % 2 == 0, "token pairs");
+#pragma unroll
+        for (int t = 0; t < TPG; t += 2) {
+            bf16x8 h8, l8;
+            split8(qk[t], qk[t + 1], ne, h8, l8);
+            const u32x4 hw = __builtin_bit_cast(u32x4, h8), lw = __builtin_bit_cast(u32x4, l8);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tok = tok0 + t + u;
+                const uint32_t qh = hw[2 * u], dh = hw[2 * u + 1];
+                const uint32_t ql = lw[2 * u], dl = lw[2 * u + 1];
+                *reinterpret_cast<uint32_t *>(&B.QH[tok][kc]) = qh;
+                *reinterpret_cast<uint32_t *>(&B.QL[tok][kc]) = ql;
+                *reinterpret_cast<uint32_t *>(&B.DH[tok][kc]) = dh;
+                *reinterpret_cast<uint32_t *>(&B.DL[tok][kc]) = dl;
+                const bf16x2 vh = __builtin_bit_cast(bf16x2, dh), vl = __builtin_bit_cast(bf16x2, dl);
+                kdh0[t + u] = vh[0]; kdh1[t + u] = vh[1]; kdl0[t + u] = vl[0]; kdl1[t + u] = vl[1];
+            }
         }
     }
     // Kd^T rows: this lane's TPG consecutive tokens of channels ch, ch + 1
@@ -649,7 +672,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     if constexpr (BF) {
         bf16x4 h, l;
         split4(tv, ne, h, l);
-        *reinterpret_cast<bf16x8 *>(&B.TH[j][8 * g4]) = cat(h, l);
+        *reinterpret_cast<bf16x8 *>(&B.TH[j][8 * g4]) = cat(h, h);
+        *reinterpret_cast<bf16x8 *>(&B.TL[j][8 * g4]) = cat(l, l);
     } else {
         *reinterpret_cast<OT4 *>(&B.TH[j][4 * g4]) = OT4{tv[0], tv[1], tv[2], tv[3]};
     }
@@ -709,7 +733,7 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
 
     if constexpr (C::BF) {
         // T and P of the chunk are final when the chunk starts: read first
-        const bf16x8 tt = ld8b(&B.TH[j][8 * g4]);
+        const bf16x8 th2 = ld8b(&B.TH[j][8 * g4]), tl2 = ld8b(&B.TL[j][8 * g4]);
         const bf16x8 ph2 = ld8b(&B.PH[j][8 * g4]), pl2 = ld8b(&B.PL[j][8 * g4]);
         bf16x8 kd[C::DK / 16];
         auto load_kd = [&]() {
@@ -732,10 +756,8 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                     load_kd();
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                bf16x4 h0, l0, h1, l1;
-                split4(S[2 * s], ne, h0, l0);
-                split4(S[2 * s + 1], ne, h1, l1);
-                const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
+                bf16x8 sh, sl;
+                split8(S[2 * s], S[2 * s + 1], ne, sh, sl);
                 // stored positions 32 s + 8 g4 .. + 7 hold exactly these channels
                 const int kk = 32 * s + 8 * g4;
                 const bf16x8 nk = s == 0 ? ah.nk : ld8b(&B.NK[j][kk]);
@@ -760,11 +782,14 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             o = mma32(cat(hh, ll), cat(qh, qh), o);          // (Sh + Sl) Qh
             o = mma32(cat(hh, ll), cat(ql, ql), o);          // (Sh + Sl) Ql
         }
-        // U = T X with both as hi/lo pairs: (Th + Tl)(Xh + Xl)
-        bf16x8 xhh, xll, uhh, ull;
-        split_hl(x, ne, xhh, xll);
-        u = mma32(tt, xhh, zero);
-        u = mma32(tt, xll, u);
+        // U = T X with both as hi/lo pairs: [Th | Th] and [Tl | Tl] against
+        // [Xh; Xl]
+        bf16x8 uhh, ull;
+        bf16x4 xh, xl;
+        split4(x, ne, xh, xl);
+        const bf16x8 xhl = cat(xh, xl);
+        u = mma32(th2, xhl, zero);
+        u = mma32(tl2, xhl, u);
         bf16x4 uh, ul;
         split4(u, ne, uh, ul);
         uhh = cat(uh, uh);
