@@ -59,8 +59,6 @@ void kda_decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 
     // 2. per-channel vectors into LDS
     __shared__ float s_a[DK], s_k[DK], s_q[DK];
-    __shared__ f32x4 s_pk[Sh::RP][Sh::CB], s_pq[Sh::RP][Sh::CB];
-    __shared__ float s_kq[Sh::RP];
     for (int i = tid; i < DK; i += Sh::NT) {
         s_a[i] = fast_exp2(g[nh * DK + i] * LOG2E);
         s_k[i] = Elem<TI>::ld(k + nh * DK + i);
@@ -82,22 +80,70 @@ void kda_decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         pq += s[p] * qi;
         kq += ki * qi;
     }
-    s_pk[r0][cb] = pk;
-    s_pq[r0][cb] = pq;
-    if (cb == 0) s_kq[r0] = kq;
-    __syncthreads();
-
-    f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-    float kqt = 0.f;
+    // 4. column sums of the partials, delta u = beta (v - S'^T k), o
+    f32x4 u;
+    if constexpr (Sh::CB == 32) {
+        // The two 32-lane halves of a wave hold the same columns (rows r0
+        // and r0 + 1): one register swap adds them.  One half wave then adds
+        // the per-wave sums, writes o and publishes u.  Compared with every
+        // thread adding all RP row partials from LDS, this cuts the LDS
+        // reads about twelvefold.
+        constexpr int NWV = Sh::NT / WAVE;
+        __shared__ f32x4 s_wk[NWV][32], s_wq[NWV][32], s_u[32];
+        __shared__ float s_wkq[NWV];
+        const int w = tid / WAVE, l = tid % WAVE;
+        f32x4 wk, wq;
 #pragma unroll
-    for (int r = 0; r < Sh::RP; ++r) {
-        ks += s_pk[r][cb];
-        qs += s_pq[r][cb];
-        kqt += s_kq[r];
+        for (int e = 0; e < 4; ++e) {
+            float lo, hi;
+            half_pair(pk[e], lo, hi);
+            wk[e] = lo + hi;
+            half_pair(pq[e], lo, hi);
+            wq[e] = lo + hi;
+        }
+        float klo, khi;
+        half_pair(kq, klo, khi);
+        if (l < 32) {
+            s_wk[w][l] = wk;
+            s_wq[w][l] = wq;
+        }
+        if (l == 0) s_wkq[w] = klo + khi;
+        __syncthreads();
+        if (tid < 32) {                  // cb == tid
+            f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+            float kqt = 0.f;
+#pragma unroll
+            for (int r = 0; r < NWV; ++r) {
+                ks += s_wk[r][tid];
+                qs += s_wq[r][tid];
+                kqt += s_wkq[r];
+            }
+            const f32x4 uu = b * (vv - ks);
+            s_u[tid] = uu;
+            Elem<TO>::st4(o + nh * DV + 4 * cb, qs + uu * kqt);
+        }
+        __syncthreads();
+        u = s_u[cb];
+    } else {
+        __shared__ f32x4 s_pk[Sh::RP][Sh::CB], s_pq[Sh::RP][Sh::CB];
+        __shared__ float s_kq[Sh::RP];
+        s_pk[r0][cb] = pk;
+        s_pq[r0][cb] = pq;
+        if (cb == 0) s_kq[r0] = kq;
+        __syncthreads();
+        f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
+        float kqt = 0.f;
+#pragma unroll
+        for (int r = 0; r < Sh::RP; ++r) {
+            ks += s_pk[r][cb];
+            qs += s_pq[r][cb];
+            kqt += s_kq[r];
+        }
+        u = b * (vv - ks);
+        if (r0 == 0) Elem<TO>::st4(o + nh * DV + 4 * cb, qs + u * kqt);
     }
 
-    // 4. delta, rank-1 write, read-out
-    const f32x4 u = b * (vv - ks);
+    // 5. rank-1 write
 #pragma unroll
     for (int p = 0; p < Sh::R; ++p) {
         const int i = r0 + p * Sh::RP;
@@ -105,7 +151,6 @@ void kda_decode_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         __builtin_nontemporal_store(s[p] + ki * u,
                                     reinterpret_cast<f32x4 *>(Sh_ + i * DV + 4 * cb));
     }
-    if (r0 == 0) Elem<TO>::st4(o + nh * DV + 4 * cb, qs + u * kqt);
 }
 
 template <typename TI, typename TO, int DK, int DV>

@@ -153,7 +153,7 @@ def test_deterministic():
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 128), (128, 128), (128, 32)])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 128), (32, 64), (64, 128), (128, 128), (128, 32)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_decode_small(dk, dv, dtype):
     from oracle.recurrence import kda_decode_step as ref_step
