@@ -66,15 +66,18 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_alg_bytes: int):
+def measured_traffic(workload: str):
     """HBM bytes per prefill launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source."""
+    summary, if it was taken on the current kernel source and on this
+    workload (None otherwise)."""
     try:
         with open(PROFILE_PMC) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != source_hash():
+        return None
+    if rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -209,7 +212,7 @@ def main():
     alg_b = prefill_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs, S0 is not None)
     alg_f = prefill_flops(tokens, wl.H, wl.dk, wl.dv)
     achieved = alg_b / pf_s / 1e9
-    traffic = measured_traffic(alg_b)
+    traffic = measured_traffic(args.workload)
     out = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, 1xMI355X, % roofline",
         "value": tokens / pf_s,

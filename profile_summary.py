@@ -5,8 +5,9 @@ under profiles/.
       kernel-trace statistics (rocprofv3 --kernel-trace --stats) as a table
   python profile_summary.py pmc <fetch_dir> <write_dir> <copy_mib> <out.json> "<commands>"
       HBM bytes per prefill launch from one FETCH_SIZE and one WRITE_SIZE
-      pass, each scaled by what the same counter reads for the plain device
-      copy of <copy_mib> MiB that `bench.py --calib-copy-mib` runs
+      pass over the default bench workload (prefill), each scaled by what the
+      same counter reads for the plain device copy of <copy_mib> MiB that
+      `bench.py --calib-copy-mib` runs
 
 The JSON records the hash of the kernel sources it was taken on; bench.py
 reports the traffic only while that hash matches.
@@ -81,7 +82,7 @@ def pmc(fetch_dir, write_dir, copy_mib, out_json, commands):
     cf, cw = _pick(fe, is_copy) * 1024, _pick(wr, is_copy) * 1024
     pf, pw = _pick(fe, is_pf) * 1024, _pick(wr, is_pf) * 1024
     rf, rw = copy_bytes / cf, copy_bytes / cw
-    rec = {"kernel": PREFILL,
+    rec = {"kernel": PREFILL, "workload": "prefill",
            "fetch_bytes_raw": pf, "write_bytes_raw": pw,
            "copy_bytes": copy_bytes, "copy_fetch_raw": cf, "copy_write_raw": cw,
            "fetch_scale": rf, "write_scale": rw,
