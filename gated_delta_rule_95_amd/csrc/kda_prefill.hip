@@ -46,8 +46,9 @@
 // accumulation; the state stays fp32 in registers.  Operands whose rounding
 // shows up in o or S (Sd, QE, T, X, U, P and Kd) are bf16 hi + lo pairs; a
 // pair-by-pair product (h1 + l1)(h2 + l2) is two 16x16x32 MFMAs whose K slots
-// hold [h1 | l1] against [h2 | h2] and [l2 | l2] (three for QE Sd, where the
-// K slots are all channels), leaving a relative error near 2^-16.  Only -KE
+// hold [h1 | l1] against [h2 | h2] and [l2 | l2], or [h1 | h1] and [l1 | l1]
+// against [h2 | l2] (three for QE Sd, where the K slots are all channels),
+// leaving a relative error near 2^-16.  Only -KE
 // (in X and A) is a single bf16.  fp32 inputs run the same schedule on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32).
 #include <type_traits>
