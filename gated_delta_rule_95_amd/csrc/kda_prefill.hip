@@ -831,6 +831,38 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
 }
 
 // ---------------------------------------------------------------------------
+// Longest sequences first.  The sequences of a packed batch can differ in
+// length by orders of magnitude, and workgroups start in index order; a long
+// sequence whose workgroups start late then sets the end of the launch.
+// Dealing the sequences out longest first (ties by index) leaves the short
+// ones for the tail.  The device holds cu_seqlens, so every wave ranks the
+// sequences itself: lane l scores candidates l and l + 64, and the rank-r
+// sequence is the one candidate whose score is r (a permutation, whatever
+// the lengths).  Cost: n_seqs steps per wave, so only up to kLptMaxSeqs.
+// ---------------------------------------------------------------------------
+constexpr int kLptMaxSeqs = 128;
+__device__ __forceinline__ int seq_of_rank(const int32_t *__restrict__ cu, int n_seqs, int r,
+                                           int lane)
+{
+    auto len = [&](int s) -> int {
+        if (s >= n_seqs) return -1;
+        const int d = cu[s + 1] - cu[s];
+        return d < 0 ? 0 : d;
+    };
+    const int s0 = lane, s1 = lane + 64;
+    const int L0 = len(s0), L1 = len(s1);
+    int k0 = 0, k1 = 0;                  // sequences ahead of s0 and s1
+    for (int t = 0; t < n_seqs; ++t) {
+        const int Lt = __builtin_amdgcn_readlane(t < 64 ? L0 : L1, t & 63);
+        k0 += (Lt > L0 || (Lt == L0 && t < s0)) ? 1 : 0;
+        k1 += (Lt > L1 || (Lt == L1 && t < s1)) ? 1 : 0;
+    }
+    const uint64_t m0 = __ballot(L0 >= 0 && k0 == r);
+    const uint64_t m1 = __ballot(L1 >= 0 && k1 == r);
+    return m0 ? __ffsll((unsigned long long)m0) - 1 : 64 + __ffsll((unsigned long long)m1) - 1;
+}
+
+// ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
@@ -855,7 +887,13 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     const int vb = rest % NB;
     const int chain = (rest / NB) * 8 + xcd;
     if (chain >= n_chains) return;
-    const int n = chain / H, h = chain % H;
+    const int h = chain % H;
+    int n = chain / H;
+    if (cu_seqlens && n_chains / H <= kLptMaxSeqs)
+        n = __builtin_amdgcn_readfirstlane(seq_of_rank(cu_seqlens, n_chains / H, n, threadIdx.x & 63));
+    // the state slot of (sequence n, head h); the dispatch index `chain`
+    // differs from it once sequences are dealt longest first
+    const int64_t state_of = (int64_t)n * H + h;
     int64_t bos, T;
     if (cu_seqlens) {
         bos = cu_seqlens[n];
@@ -963,7 +1001,7 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     } else {
         // consumer state: S[:, col_base + 16 wave + j], rows 16 t + 4 g4 + i
         f32x4 S[DK / 16];
-        const int64_t sbase = (int64_t)chain * DK * DV + col_base + 16 * wave + j;
+        const int64_t sbase = state_of * DK * DV + col_base + 16 * wave + j;
 #pragma unroll
         for (int t = 0; t < DK / 16; ++t)
 #pragma unroll

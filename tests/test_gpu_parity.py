@@ -150,6 +150,25 @@ def test_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+@pytest.mark.parametrize("n_seqs", [5, 70, 130])
+def test_dispatch_order_keeps_state_slots(n_seqs):
+    """Packed batches of up to 128 sequences are dealt to workgroups longest
+    first (above 128 in index order).  Lengths increasing with the index, so
+    the order reverses; every sequence has its own S0 and must read and write
+    exactly its own state slot and token range.  70 sequences cover the
+    second rank register (sequences 64 and up), 130 the index order."""
+    lengths = [1 + (3 * i) % 37 + i // 4 for i in range(n_seqs)]
+    lengths[n_seqs // 2] = 0
+    b = random_batch(41 + n_seqs, lengths, H=2, dk=32, dv=32, bf16=False)
+    say("dispatch order", n_seqs)
+    o_ref, ST_ref = oracle(b)
+    o, ST = run_fwd(b, torch.float32, out_dtype=torch.float32)
+    assert err(o, o_ref) <= 1e-4, err(o, o_ref)
+    for n in range(n_seqs):
+        assert err(ST[n], ST_ref[n]) <= 1e-4, (n, err(ST[n], ST_ref[n]))
+    assert np.array_equal(ST[n_seqs // 2], b["s0"][n_seqs // 2])
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
