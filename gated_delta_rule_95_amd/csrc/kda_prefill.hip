@@ -194,8 +194,8 @@ struct Cfg {
     static constexpr int DK = DK_;
     static constexpr int NW = NW_;                 // consumer waves
     // builder waves: up to four, each with at least 16 key channels; the
-    // count does not depend on the block width, so narrow blocks (used when
-    // there are too few chains to fill the device) keep the build rate
+    // count does not depend on the block width, so narrow blocks (d_v of 16
+    // or 32) keep the build rate
     static constexpr int NBW = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
