@@ -150,7 +150,7 @@ def test_deterministic():
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
-@pytest.mark.parametrize("n_seqs", [5, 70, 130])
+@pytest.mark.parametrize("n_seqs", [5, 64, 70, 128, 130])
 def test_dispatch_order_keeps_state_slots(n_seqs):
     """Packed batches of up to 128 sequences are dealt to workgroups longest
     first (above 128 in index order).  Lengths increasing with the index, so
