@@ -5,18 +5,20 @@ device memory and the current HIP stream; every step of KDA runs in the
 library's hand-written gfx950 kernels.  Names follow the C ABI:
 
     kda_fwd_chunked(q, k, v, g, beta, S0=None, cu_seqlens=None, ...) -> (o, S_T)
+    kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, dtype) -> int
     kda_decode_step(q, k, v, g, beta, S, ...) -> o        (S updated in place)
 """
 from __future__ import annotations
 
-from typing import Optional, Tuple
+from typing import Optional, Tuple, Union
 
 import torch
 
 from . import _lib
 from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
 
-__all__ = ["kda_fwd_chunked", "kda_decode_step", "KDAError", "version", "library_path"]
+__all__ = ["kda_fwd_chunked", "kda_fwd_workspace_bytes", "kda_decode_step", "KDAError",
+           "version", "library_path"]
 
 
 def library_path() -> str:
@@ -56,13 +58,21 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def kda_fwd_workspace_bytes(n_seqs: int, n_tokens: int, H: int, d_k: int, d_v: int,
+                            dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of workspace with which kda_fwd_chunked may take the
+    sequence-split path for these sizes on the current device (0: none)."""
+    return int(_lib.load().kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, _dt(dtype)))
+
+
 def kda_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                     beta: torch.Tensor, S0: Optional[torch.Tensor] = None,
                     cu_seqlens: Optional[torch.Tensor] = None,
                     out_dtype: Optional[torch.dtype] = None,
                     output_final_state: bool = True,
                     o: Optional[torch.Tensor] = None,
-                    S_T: Optional[torch.Tensor] = None
+                    S_T: Optional[torch.Tensor] = None,
+                    workspace: Union[None, bool, torch.Tensor] = False,
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.
 
@@ -70,6 +80,10 @@ def kda_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     g    : [..., H, d_k] fp32 log-decay in [-5, 0];  beta : [..., H] fp32
     S0   : [n_seqs, H, d_k, d_v] fp32 or None
     cu_seqlens : int32 [n_seqs + 1] on the device (packed input only)
+    workspace  : None or True -> a torch buffer of kda_fwd_workspace_bytes is
+                 allocated here when that size is nonzero (the library itself
+                 allocates nothing); False -> no workspace (single pass);
+                 a contiguous uint8 device tensor -> used as given
     Returns (o [same leading shape, d_v], S_T [n_seqs, H, d_k, d_v] or None).
     """
     dev = q.device
@@ -110,9 +124,19 @@ def kda_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     elif S_T is not None:
         _need(S_T, "S_T", dtype=torch.float32, shape=(n_seqs, H, dk, dv), device=dev)
     lib = _lib.load()
+    ws, ws_bytes = None, 0
+    if isinstance(workspace, torch.Tensor):
+        _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+        ws, ws_bytes = workspace, workspace.numel()
+    elif workspace is None or workspace is True:
+        need = 0 if (cu_seqlens is not None and n_seqs > 1) else \
+            int(lib.kda_fwd_workspace_bytes(n_seqs, N, H, dk, dv, in_dt))
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws_bytes = need
     st = lib.kda_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
                              _ptr(cu_seqlens), n_seqs, N, H, dk, dv, in_dt, _dt(od),
-                             _ptr(o), _ptr(S_T), _stream(dev))
+                             _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes, _stream(dev))
     _lib.check(st)
     return o, S_T
 

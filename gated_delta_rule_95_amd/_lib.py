@@ -41,9 +41,12 @@ def load() -> ctypes.CDLL:
                 "(or __graft_entry__.build()) first. There is no CPU fallback.")
         lib = ctypes.CDLL(LIB_PATH)
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        SZ = ctypes.c_size_t
         lib.kda_fwd_chunked.restype = ctypes.c_int
         lib.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
-                                        ctypes.c_int, ctypes.c_int, P, P, P]
+                                        ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+        lib.kda_fwd_workspace_bytes.restype = SZ
+        lib.kda_fwd_workspace_bytes.argtypes = [I32, I64, I32, I32, I32, ctypes.c_int]
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                         ctypes.c_int, ctypes.c_int, P, P]

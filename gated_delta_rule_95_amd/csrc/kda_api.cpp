@@ -88,17 +88,11 @@ kda_status hip_status(hipError_t e, const char *what)
     return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-}  // namespace
-
-KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
-                                   const float *g, const float *beta, const float *S0,
-                                   const int32_t *cu_seqlens, int32_t n_seqs,
-                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
-                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
-                                   float *S_T, kda_stream_t stream)
+// Size checks shared by kda_fwd_chunked and kda_fwd_workspace_bytes.
+kda_status check_fwd_sizes(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                           int32_t d_v, bool packed)
 {
     kda_status s;
-    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
     if ((s = check_dims(H, d_k, d_v)) != KDA_OK) return s;
     if (n_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "n_seqs must be >= 0 (got %d)", n_seqs);
     if (n_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens must be >= 0");
@@ -108,19 +102,77 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     if ((int64_t)H * (d_k > d_v ? d_k : d_v) >= ((int64_t)1 << 25))
         return fail(KDA_ERR_INVALID_ARG, "H * d must be below 2^25 (16 rows of a tensor "
                                          "must stay below 2^31 bytes)");
-    if (n_seqs == 0) {
-        if (n_tokens != 0) return fail(KDA_ERR_INVALID_ARG, "n_tokens > 0 with n_seqs == 0");
-        return ok();
-    }
-    int32_t seqlen = 0;
-    if (!cu_seqlens) {
-        if (n_tokens % n_seqs)
-            return fail(KDA_ERR_INVALID_ARG,
-                        "without cu_seqlens n_tokens (%lld) must be a multiple of n_seqs (%d)",
-                        (long long)n_tokens, n_seqs);
-        seqlen = (int32_t)(n_tokens / n_seqs);
-    } else if (!aligned(cu_seqlens, 4)) {
+    if (n_seqs == 0 && n_tokens != 0)
+        return fail(KDA_ERR_INVALID_ARG, "n_tokens > 0 with n_seqs == 0");
+    if (n_seqs > 0 && !packed && n_tokens % n_seqs)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "without cu_seqlens n_tokens (%lld) must be a multiple of n_seqs (%d)",
+                    (long long)n_tokens, n_seqs);
+    return KDA_OK;
+}
+
+kda::PrefillArgs size_args(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                           int32_t d_v, bool in_bf16, const int32_t *cu_seqlens)
+{
+    kda::PrefillArgs a{};
+    a.cu_seqlens = cu_seqlens;
+    a.n_seqs = n_seqs;
+    a.n_tokens = n_tokens;
+    a.seqlen = (!cu_seqlens && n_seqs > 0) ? (int32_t)(n_tokens / n_seqs) : 0;
+    a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_bf16;
+    return a;
+}
+
+constexpr size_t kWorkspaceAlign = 256;
+
+}  // namespace
+
+KDA_API size_t kda_fwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H,
+                                       int32_t d_k, int32_t d_v, kda_dtype in_dtype)
+{
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16) return 0;
+    if (check_fwd_sizes(n_seqs, n_tokens, H, d_k, d_v, false) != KDA_OK) return 0;
+    if (n_seqs == 0 || n_tokens == 0) return 0;
+    return kda::prefill_workspace_bytes(
+        size_args(n_seqs, n_tokens, H, d_k, d_v, in_dtype == KDA_BF16, nullptr));
+}
+
+namespace {
+// a non-null placeholder: only its being set matters to the size planner
+const int32_t kPackedMarker = 0;
+}  // namespace
+
+KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t n_seqs,
+                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   float *S_T, void *workspace, size_t workspace_bytes,
+                                   kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
+    if ((s = check_fwd_sizes(n_seqs, n_tokens, H, d_k, d_v, cu_seqlens != nullptr)) != KDA_OK)
+        return s;
+    if (cu_seqlens && !aligned(cu_seqlens, 4))
         return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+    if (!workspace && workspace_bytes != 0)
+        return fail(KDA_ERR_INVALID_ARG, "workspace is NULL but workspace_bytes is %zu",
+                    workspace_bytes);
+    if (workspace && !aligned(workspace, kWorkspaceAlign))
+        return fail(KDA_ERR_INVALID_ARG, "workspace is not %zu-byte aligned", kWorkspaceAlign);
+    if (n_seqs == 0) return ok();
+    const int32_t seqlen = cu_seqlens ? 0 : (int32_t)(n_tokens / n_seqs);
+    size_t need = 0;
+    if (workspace) {
+        need = kda::prefill_workspace_bytes(
+            size_args(n_seqs, n_tokens, H, d_k, d_v, in_dtype == KDA_BF16,
+                      cu_seqlens ? &kPackedMarker : nullptr));
+        if (workspace_bytes < need)
+            return fail(KDA_ERR_INVALID_ARG,
+                        "workspace_bytes %zu is below the %zu bytes kda_fwd_workspace_bytes "
+                        "gives for these sizes", workspace_bytes, need);
     }
     const bool have_tokens = n_tokens > 0;
     const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
@@ -138,9 +190,13 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     for (int i = 0; i < 6; ++i) {
         if (overlap(o, o_bytes, ins[i], in_sz[i]) || overlap(S_T, st_bytes, ins[i], in_sz[i]))
             return fail(KDA_ERR_INVALID_ARG, "an output buffer overlaps an input buffer");
+        if (overlap(workspace, need, ins[i], in_sz[i]))
+            return fail(KDA_ERR_INVALID_ARG, "the workspace overlaps an input buffer");
     }
     if (overlap(o, o_bytes, S_T, st_bytes))
         return fail(KDA_ERR_INVALID_ARG, "o overlaps S_T");
+    if (overlap(workspace, need, o, o_bytes) || overlap(workspace, need, S_T, st_bytes))
+        return fail(KDA_ERR_INVALID_ARG, "the workspace overlaps an output buffer");
 
     kda::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0;
@@ -148,6 +204,8 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
     a.o = o; a.S_T = S_T; a.stream = stream;
+    a.workspace = need ? workspace : nullptr;
+    a.workspace_bytes = need;
     return hip_status(kda::launch_prefill(a), "kda_fwd_chunked launch");
 }
 

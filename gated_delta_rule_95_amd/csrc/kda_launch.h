@@ -28,10 +28,16 @@ struct PrefillArgs {
     bool in_bf16, out_bf16;
     void *o;
     float *S_T;
+    void *workspace;             // caller scratch (nullptr: single pass)
+    size_t workspace_bytes;
     void *stream;
 };
 
 hipError_t launch_decode(const DecodeArgs &a);
+// Bytes of workspace the sequence-split path needs for these sizes on the
+// current device (0: the single-pass kernel is used).  Reads only the size
+// fields of `a` (and whether cu_seqlens is set).
+size_t prefill_workspace_bytes(const PrefillArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
 
 }  // namespace kda

@@ -51,7 +51,11 @@
 // leaving a relative error near 2^-16.  Only -KE
 // (in X and A) is a single bf16.  fp32 inputs run the same schedule on the
 // fp32 matrix cores (v_mfma_f32_16x16x4_f32).
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <type_traits>
+#include <vector>
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -295,22 +299,23 @@ __device__ __forceinline__ float elem(typename Raw<C>::P2 x, int i)
 // ---------------------------------------------------------------------------
 // loads of one chunk's raw inputs through buffer resources bounded by the
 // chunk's real tokens: padded tokens read k = q = v = 0, g = 0, beta = 0,
-// an exact identity transition.  ntok may be <= 0 (nothing is read).
+// an exact identity transition.  ntok may be <= 0 (nothing is read); the
+// values are read for ntok_v tokens (ntok, or 0 for zero values).
 // ---------------------------------------------------------------------------
 template <class C, typename TI>
 __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
                                          const TI *__restrict__ k, const TI *__restrict__ v,
                                          const float *__restrict__ g,
                                          const float *__restrict__ beta, int64_t tok_base,
-                                         int ntok, int H, int h, int DV, int col_base,
-                                         int wave, int lane, int tid)
+                                         int ntok, int ntok_v, int H, int h, int DV,
+                                         int col_base, int wave, int lane, int tid)
 {
     constexpr int ES = sizeof(TI);
     const int rowk = H * C::DK, rowv = H * DV;
     const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * ES);
     const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * ES);
     const rsrc_t rg = make_rsrc(g + tok_base * rowk, ntok * rowk * 4);
-    const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok * rowv * ES);
+    const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok_v * rowv * ES);
     const rsrc_t rb = make_rsrc(beta + tok_base * H, ntok * H * 4);
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
@@ -348,23 +353,16 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
 
 // ---------------------------------------------------------------------------
 // Inclusive prefix sum over the NG token groups of a wave (group tg = lane /
-// CPW, one value per lane and group) and the total over all groups.  With 2
-// or 4 groups (halves or 16-lane rows of the wave) the exchanges are the
-// register swaps across half waves and row pairs (half_pair, row_pair): no
-// LDS round trip.
+// CPW, one value per lane and group) and the total over all groups.  The
+// builder mapping gives NG = 4 (d_k = 128: the groups are the 16-lane rows,
+// exchanged with the register swaps across row pairs and half waves, no LDS
+// round trip) or NG = 8 (d_k <= 64: eight-lane groups, lane shuffles).
 // ---------------------------------------------------------------------------
 template <int NG, int CPW>
 __device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &tot)
 {
-    if constexpr (NG == 1) {
-        incl = x;
-        tot = x;
-    } else if constexpr (NG == 2) {
-        float lo, hi;                    // the lower and the upper half's value
-        half_pair(x, lo, hi);
-        tot = lo + hi;
-        incl = tg ? tot : x;
-    } else if constexpr (NG == 4) {
+    static_assert(NG == 4 || NG == 8, "builder token groups");
+    if constexpr (NG == 4) {
         float ev, od;                    // the even and odd row of this row pair
         row_pair(x, ev, od);
         const float pair = ev + od;
@@ -720,7 +718,6 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                                          const Ahead<C> &ah, int wave, int lane)
 {
     const int j = lane & 15, g4 = lane >> 4;
-    const int vc = 16 * wave + j;           // column inside the block
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const NegEye ne = neg_eye(lane);
     f32x4 x, u, o = zero;
@@ -863,53 +860,145 @@ __device__ __forceinline__ int seq_of_rank(const int32_t *__restrict__ cu, int n
 }
 
 // ---------------------------------------------------------------------------
+// Launch parameters.  Every workgroup runs one job: a token range of one
+// (sequence, head) chain and one block of BV state columns.
+//
+// Without a sequence split (nseg == 1) a job is a whole sequence and one
+// block of the d_v value columns.
+//
+// With a split, each sequence's tokens are cut into segment 0 (the first
+// len0 tokens) and segments 1 .. nseg-1 (lenS tokens each, the last one
+// possibly shorter).  Segment 0 runs from S0 as usual and leaves its final
+// state as the entry state of segment 1.  A later segment runs from a zero
+// state and carries, next to its d_v value columns, the d_k columns of the
+// segment's transition: those start from the identity with zero values, so
+// they evolve into M = Phi (the product of the segment's per-token maps
+// S -> (I - b k k^T) Diag(alpha) S) and their outputs are R_t = Phi_t^T q_t.
+// Then  S_end = M S_entry + S~  and  o_t = o~_t + S_entry^T R_t  for every
+// token t of the segment, where S~ and o~ come from the value columns.  The
+// scan and the correction kernels below apply these once the entry states
+// are known.  (Affine summary of a segment and a prefix scan over segments:
+// K3-on-TPU essay, blog.higcp.com, the section on the existing TPU kernel;
+// used across compute units of one device, the intra-device sequence-split
+// regime of the same essay's "KDA + Gated MLA" costs section, item (3).)
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO>
+struct Params {
+    const TI *q, *k, *v;
+    const float *g, *beta, *S0;
+    const int32_t *cu_seqlens;   // nullptr: equal lengths seqlen
+    TO *o;
+    float *S_T;
+    int32_t seqlen, n_tokens, n_chains, chains8, H;
+    // sequence split (nseg == 1: none; only with cu_seqlens == nullptr)
+    int32_t nseg, len0, lenS;
+    float *sumst;   // [chain][nseg-1][d_k][d_v + d_k]  final states of segments 1..
+    float *entry;   // [chain][nseg-1][d_k][d_v]        entry states of segments 1..
+    float *o0;      // [n_seqs][seqlen - len0][H][d_v]  zero-start outputs o~
+    float *rq;      // [n_seqs][seqlen - len0][H][d_k]  pulled-back queries R
+};
+
+// ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
 __global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF>::NT), 1)
-void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
-                        const TI *__restrict__ v, const float *__restrict__ g,
-                        const float *__restrict__ beta, const float *__restrict__ S0,
-                        const int32_t *__restrict__ cu_seqlens, int32_t seqlen,
-                        int32_t n_chains, int32_t H, TO *__restrict__ o,
-                        float *__restrict__ S_T)
+void kda_prefill_kernel(const Params<TI, TO> p)
 {
     using C = Cfg<TI, DK, NW, NBUF>;
-    constexpr int NB = DV / C::BV;
+    constexpr int NB = DV / C::BV;               // value column blocks of a chain
+    constexpr int NA = NB + DK / C::BV;          // ... plus transition blocks (split)
     constexpr int LAG = NBUF - 1;            // build runs LAG chunks ahead
     __shared__ Smem<C> sm;
+    const int H = p.H;
 
-    // workgroup -> (chain, column block); the NB blocks of a chain share an
-    // XCD (workgroups are dealt round-robin over the 8 XCDs), so the chain's
-    // q/k/g are fetched from HBM once and re-read from that XCD's L2.
-    const int bid = blockIdx.x;
+    // Workgroup -> job.  Jobs come in groups, one per segment, longest
+    // first (segment 0, then segments 1, 2, ...), each group chains8 x
+    // (blocks per chain) workgroups.  Inside a group the blocks of a chain
+    // share an XCD (workgroups are dealt round-robin over the 8 XCDs), so
+    // the chain's q/k/g are fetched from HBM once and re-read from that
+    // XCD's L2.
+    int bid = blockIdx.x, seg = 0, W = NB;
+    if (bid >= p.chains8 * NB) {
+        const int r = bid - p.chains8 * NB;
+        seg = 1 + r / (p.chains8 * NA);
+        bid = r % (p.chains8 * NA);
+        W = NA;
+    }
     const int xcd = bid & 7, rest = bid >> 3;
-    const int vb = rest % NB;
-    const int chain = (rest / NB) * 8 + xcd;
-    if (chain >= n_chains) return;
+    const int vb = rest % W;
+    const int chain = (rest / W) * 8 + xcd;
+    if (chain >= p.n_chains) return;
     const int h = chain % H;
     int n = chain / H;
-    if (cu_seqlens && n_chains / H <= kLptMaxSeqs)
-        n = __builtin_amdgcn_readfirstlane(seq_of_rank(cu_seqlens, n_chains / H, n, threadIdx.x & 63));
+    if (p.cu_seqlens && p.n_chains / H <= kLptMaxSeqs)
+        n = __builtin_amdgcn_readfirstlane(
+            seq_of_rank(p.cu_seqlens, p.n_chains / H, n, threadIdx.x & 63));
     // the state slot of (sequence n, head h); the dispatch index `chain`
     // differs from it once sequences are dealt longest first
     const int64_t state_of = (int64_t)n * H + h;
     int64_t bos, T;
-    if (cu_seqlens) {
-        bos = cu_seqlens[n];
-        T = (int64_t)cu_seqlens[n + 1] - bos;
-        if (T < 0) T = 0;
+    if (p.cu_seqlens) {
+        // entries are clamped into [0, n_tokens]: a cu_seqlens that breaks
+        // its contract changes the result, never the addresses touched
+        const int32_t c0 = p.cu_seqlens[n], c1 = p.cu_seqlens[n + 1];
+        const int32_t a0 = c0 < 0 ? 0 : (c0 > p.n_tokens ? p.n_tokens : c0);
+        const int32_t a1 = c1 < 0 ? 0 : (c1 > p.n_tokens ? p.n_tokens : c1);
+        bos = a0;
+        T = a1 > a0 ? a1 - a0 : 0;
     } else {
-        bos = (int64_t)n * seqlen;
-        T = seqlen;
+        bos = (int64_t)n * p.seqlen;
+        T = p.seqlen;
     }
+    // this job's tokens, its value source, entry state, output and final
+    // state (all wave-uniform)
+    const bool trans = vb >= NB;                 // transition columns of a later segment
+    const int col_base = (trans ? vb - NB : vb) * C::BV;
+    int64_t t0 = 0;                              // first token, relative to bos
+    int s0_mode = p.S0 ? 1 : 0;                  // 0 zero, 1 load, 2 identity
+    const float *s0p = p.S0 + state_of * DK * DV + col_base;
+    int s0_row = DV;
+    char *obase = reinterpret_cast<char *>(p.o);
+    int64_t orow = (int64_t)H * DV * sizeof(TO), ocol = ((int64_t)h * DV + col_base) * sizeof(TO);
+    bool out_f32 = sizeof(TO) == 4;
+    float *stp = p.S_T ? p.S_T + state_of * DK * DV + col_base : nullptr;
+    int st_row = DV;
+    if (p.nseg > 1) {
+        if (seg == 0) {
+            T = T < p.len0 ? T : p.len0;
+            stp = p.entry + state_of * (p.nseg - 1) * DK * DV + col_base;
+        } else {
+            t0 = p.len0 + (int64_t)(seg - 1) * p.lenS;
+            const int64_t rem = T - t0;
+            T = rem < 0 ? 0 : (rem < p.lenS ? rem : p.lenS);
+            const int64_t aug = (int64_t)n * (p.seqlen - p.len0) + (t0 - p.len0);
+            s0_mode = trans ? 2 : 0;
+            st_row = DV + DK;
+            stp = p.sumst + (state_of * (p.nseg - 1) + seg - 1) * DK * (DV + DK) +
+                  (trans ? DV : 0) + col_base;
+            out_f32 = true;
+            if (trans) {
+                obase = reinterpret_cast<char *>(p.rq + aug * H * DK);
+                orow = (int64_t)H * DK * 4;
+                ocol = ((int64_t)h * DK + col_base) * 4;
+            } else {
+                obase = reinterpret_cast<char *>(p.o0 + aug * H * DV);
+                orow = (int64_t)H * DV * 4;
+                ocol = ((int64_t)h * DV + col_base) * 4;
+            }
+        }
+    }
+    if (seg == 0) obase += bos * orow;
+    bos += t0;
     // wave-uniform values are made visibly uniform (readfirstlane) so that
     // branches on them are scalar and the buffer resources built from them
     // live in scalar registers
     bos = uniform64(bos);
     const int Tn = __builtin_amdgcn_readfirstlane((int)T);     // < 2^31 - 64 (host)
     const int nch = (Tn + 15) / 16;
-    const int col_base = vb * C::BV;
+    // transition columns have zero values: their value loads get an empty
+    // buffer range (they read zeros, as the ragged tail does)
+    const bool v_on = !trans;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -950,8 +1039,8 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
         constexpr int NR = C::NR;
         Raw<C> r[NR];
         auto load = [&](Raw<C> &x, int cc) {
-            load_raw<C>(x, q, k, v, g, beta, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, DV,
-                        col_base, bw, lane, btid);
+            load_raw<C>(x, p.q, p.k, p.v, p.g, p.beta, bos + 16 * (int64_t)cc, ntok_of(cc),
+                        v_on ? ntok_of(cc) : 0, H, h, DV, col_base, bw, lane, btid);
         };
 #pragma unroll
         for (int i = 0; i < NR; ++i) load(r[i], i);
@@ -1001,22 +1090,26 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
     } else {
         // consumer state: S[:, col_base + 16 wave + j], rows 16 t + 4 g4 + i
         f32x4 S[DK / 16];
-        const int64_t sbase = state_of * DK * DV + col_base + 16 * wave + j;
+        const int col = 16 * wave + j;           // column inside the block
 #pragma unroll
         for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[t][i] = S0 ? S0[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * t + 4 * g4 + i;
+                S[t][i] = s0_mode == 1 ? s0p[(int64_t)row * s0_row + col]
+                        : s0_mode == 2 ? (row == col_base + col ? 1.f : 0.f) : 0.f;
+            }
         // O of chunk c is written at the start of iteration c + 1, so the
         // stores overlap the next chain instead of delaying this one.
-        const int rowo = H * DV;
         // lane (j, g4) holds O[token j][columns 16 wave + 4 g4 .. + 3]
-        const int ooff = (j * rowo + h * DV + col_base + 16 * wave + 4 * g4) * (int)sizeof(TO);
+        const int ow = (int)orow;                // < 2^31 / 16 (host)
+        const int ooff = j * ow + (int)ocol + (16 * wave + 4 * g4) * (out_f32 ? 4 : (int)sizeof(TO));
         f32x4 ov = {0.f, 0.f, 0.f, 0.f};
         auto store_o = [&](int cc) {
-            const rsrc_t ro = make_rsrc(o + (bos + 16 * (int64_t)cc) * rowo,
-                                        (cc >= 0 ? ntok_of(cc) : 0) * rowo * (int)sizeof(TO));
-            bstore4(ro, ooff, ov, TO{});
+            const rsrc_t ro = make_rsrc(obase + 16 * (int64_t)cc * orow,
+                                        (cc >= 0 ? ntok_of(cc) : 0) * ow);
+            if (out_f32) bstore4(ro, ooff, ov, float{});
+            else bstore4(ro, ooff, ov, TO{});
         };
         __syncthreads();
         __syncthreads();
@@ -1030,12 +1123,161 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
             __syncthreads();
         }
         if (nch > 0) store_o(nch - 1);
-        if (S_T) {
+        if (stp) {
 #pragma unroll
             for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_T[sbase + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
+                    stp[(int64_t)(16 * t + 4 * g4 + i) * st_row + col] = S[t][i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segment scan (sequence split): the entry states of segments 2 .. nseg-1
+// and the final state.  E_1 is segment 0's final state; then
+// E_{s+1} = M_s E_s + S~_s, with M_s and S~_s the transition and value
+// columns of segment s's final state.  fp32 throughout.  One workgroup per
+// (chain, block of 16 state columns); the columns of S are independent.
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_seg_scan_kernel(const float *__restrict__ sumst,
+                                                          float *__restrict__ entry,
+                                                          float *__restrict__ S_T,
+                                                          int32_t nseg)
+{
+    constexpr int NCB = DV / 16;
+    constexpr int PER = (DK * 16 + 255) / 256;   // state elements per thread
+    __shared__ float E[DK][17];
+    const int chain = blockIdx.x / NCB, cb = blockIdx.x % NCB;
+    const int tid = threadIdx.x;
+    const int64_t ebase = (int64_t)chain * (nseg - 1) * DK * DV + cb * 16;
+    for (int e = tid; e < DK * 16; e += 256) E[e / 16][e % 16] = entry[ebase + (e / 16) * DV + e % 16];
+    __syncthreads();
+    for (int s = 1; s < nseg; ++s) {
+        const float *A = sumst + ((int64_t)chain * (nseg - 1) + s - 1) * DK * (DV + DK);
+        float acc[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 256 * i;
+            acc[i] = 0.f;
+            if (e < DK * 16) {
+                const int r = e / 16, c = e % 16;
+                const float *Ar = A + (int64_t)r * (DV + DK);
+                float a = Ar[cb * 16 + c];
+#pragma unroll 8
+                for (int kk = 0; kk < DK; ++kk) a = __builtin_fmaf(Ar[DV + kk], E[kk][c], a);
+                acc[i] = a;
+            }
+        }
+        __syncthreads();
+        float *dst = s < nseg - 1 ? entry + ebase + (int64_t)s * DK * DV
+                   : (S_T ? S_T + (int64_t)chain * DK * DV + cb * 16 : nullptr);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 256 * i;
+            if (e < DK * 16) {
+                E[e / 16][e % 16] = acc[i];
+                if (dst) dst[(e / 16) * DV + e % 16] = acc[i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segment correction (sequence split): o_t = o~_t + E_s^T R_t for every
+// token t of segment s >= 1, E_s its entry state, stored in the output type.
+// Formed as O^T = E_s^T R^T on the bf16 matrix cores with hi/lo pairs of
+// both operands (Eh Rh + El Rh + Eh Rl per 32-deep step; the dropped El Rl
+// is near 2^-16 relative), so each lane ends with four consecutive outputs
+// of one token.  One workgroup per (chain, segment, 256 tokens); E_s^T is
+// staged in LDS as bf16 hi and lo rows.
+// ---------------------------------------------------------------------------
+template <typename TO, int DK, int DV>
+__global__ __launch_bounds__(256) void kda_seg_correct_kernel(
+    TO *__restrict__ o, const float *__restrict__ o0, const float *__restrict__ rq,
+    const float *__restrict__ entry, int32_t H, int32_t seqlen, int32_t len0, int32_t lenS,
+    int32_t nseg, int32_t tiles)
+{
+    static_assert(DK % 32 == 0 && DV % 16 == 0, "correction tiles");
+    // row stride 2 DK + 32 bytes, an odd multiple of 32: the 16-byte operand
+    // reads below are free of bank conflicts
+    constexpr int LE = DK + 16;
+    __shared__ __attribute__((aligned(16))) bf16 EH[DV][LE];
+    __shared__ __attribute__((aligned(16))) bf16 EL[DV][LE];
+    const int tile = blockIdx.x % tiles;
+    const int cs = blockIdx.x / tiles;
+    const int seg = 1 + cs % (nseg - 1);
+    const int chain = cs / (nseg - 1);            // n * H + h
+    const int n = chain / H, h = chain % H;
+    const int t0 = len0 + (seg - 1) * lenS;       // segment start inside the sequence
+    int segT = seqlen - t0;
+    segT = segT < lenS ? segT : lenS;
+    const int tb = 256 * tile;
+    if (tb >= segT) return;
+    const int ntile = segT - tb < 256 ? segT - tb : 256;
+
+    // E_s^T as hi/lo bf16: thread takes rows r, r + 1 of one column c
+    const float *E = entry + ((int64_t)chain * (nseg - 1) + seg - 1) * DK * DV;
+    for (int e = threadIdx.x; e < DK * DV / 2; e += 256) {
+        const int c = e % DV, r = 2 * (e / DV);
+        const float x0 = E[r * DV + c], x1 = E[(r + 1) * DV + c];
+        const uint32_t hw = pack2(x0, x1);
+        const bf16x2 hv = __builtin_bit_cast(bf16x2, hw);
+        const uint32_t lw = pack2(x0 - (float)hv[0], x1 - (float)hv[1]);
+        *reinterpret_cast<uint32_t *>(&EH[c][r]) = hw;
+        *reinterpret_cast<uint32_t *>(&EL[c][r]) = lw;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nn = lane & 15, kg = lane >> 4;
+    const int64_t aug0 = (int64_t)n * (seqlen - len0) + (t0 - len0) + tb;  // o~ / R row
+    const int64_t tok0 = (int64_t)n * seqlen + t0 + tb;                     // o row
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+        const int tt = 64 * it + 16 * wave;
+        if (tt >= ntile) break;
+        const int nt = ntile - tt < 16 ? ntile - tt : 16;
+        const rsrc_t rr = make_rsrc(rq + (aug0 + tt) * H * DK, nt * H * DK * 4);
+        const rsrc_t r0 = make_rsrc(o0 + (aug0 + tt) * H * DV, nt * H * DV * 4);
+        const rsrc_t ro = make_rsrc(o + (tok0 + tt) * H * DV, nt * H * DV * (int)sizeof(TO));
+        // B = R^T: lane (token nn, kg) holds R[nn][32 s + 8 kg .. + 7]
+        bf16x8 rh[DK / 32], rl[DK / 32];
+#pragma unroll
+        for (int s2 = 0; s2 < DK / 32; ++s2) {
+            const int off = ((nn * H + h) * DK + 32 * s2 + 8 * kg) * 4;
+            const f32x4 a = __builtin_bit_cast(f32x4, bload128(rr, off));
+            const f32x4 b = __builtin_bit_cast(f32x4, bload128(rr, off + 16));
+            const u32x4 hw = {pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]),
+                              pack2(b[2], b[3])};
+            rh[s2] = __builtin_bit_cast(bf16x8, hw);
+            f32x4 ra, rb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ra[i] = a[i] - (float)rh[s2][i];
+                rb[i] = b[i] - (float)rh[s2][4 + i];
+            }
+            const u32x4 lw = {pack2(ra[0], ra[1]), pack2(ra[2], ra[3]), pack2(rb[0], rb[1]),
+                              pack2(rb[2], rb[3])};
+            rl[s2] = __builtin_bit_cast(bf16x8, lw);
+        }
+#pragma unroll 2
+        for (int ct = 0; ct < DV / 16; ++ct) {
+            // lane (token nn, kg) accumulates O[nn][16 ct + 4 kg .. + 3]
+            const int ocol = (nn * H + h) * DV + 16 * ct + 4 * kg;
+            f32x4 acc = __builtin_bit_cast(f32x4, bload128(r0, ocol * 4));
+#pragma unroll
+            for (int s2 = 0; s2 < DK / 32; ++s2) {
+                const bf16x8 ah = ld8b(&EH[16 * ct + nn][32 * s2 + 8 * kg]);
+                const bf16x8 al = ld8b(&EL[16 * ct + nn][32 * s2 + 8 * kg]);
+                acc = mma32(ah, rh[s2], acc);
+                acc = mma32(al, rh[s2], acc);
+                acc = mma32(ah, rl[s2], acc);
+            }
+            bstore4(ro, ocol * (int)sizeof(TO), acc, TO{});
         }
     }
 }
@@ -1043,21 +1285,6 @@ void kda_prefill_kernel(const TI *__restrict__ q, const TI *__restrict__ k,
 // ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
-static hipError_t launch_t(const PrefillArgs &a, int64_t chains)
-{
-    using C = Cfg<TI, DK, NW, NBUF>;
-    static_assert(DV % C::BV == 0, "column blocks");
-    constexpr int NB = DV / C::BV;
-    const int64_t grid = ((chains + 7) / 8) * 8 * NB;
-    if (grid * C::NT >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // grid size limit
-    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF>), dim3((unsigned)grid),
-                       dim3(C::NT), 0, (hipStream_t)a.stream, (const TI *)a.q,
-                       (const TI *)a.k, (const TI *)a.v, a.g, a.beta, a.S0, a.cu_seqlens,
-                       a.seqlen, (int32_t)chains, a.H, (TO *)a.o, a.S_T);
-    return hipGetLastError();
-}
-
 // waves per workgroup: 16 columns per consumer wave, at most 4 consumers and
 // no more than the builder waves (each builder thread moves at most one
 // four-token column piece of the value block)
@@ -1068,30 +1295,206 @@ struct PickNW {
     static constexpr int value = byv < bydk ? byv : bydk;
 };
 
+// Sequence-split plan.  Chunk counts; the segments are chunk-aligned.
+struct SplitPlan {
+    int nseg = 1, len0 = 0, lenS = 0;            // tokens
+    size_t off_sumst = 0, off_entry = 0, off_o0 = 0, off_rq = 0, bytes = 0;
+};
+
+static int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 256;
+    return n > 0 ? n : 256;
+}
+
+// Finish time, in chunks, of the jobs one XCD runs: `cx` chains, each with
+// `nb` jobs of segment 0 (l0 chunks) and, per later segment, `na` jobs of
+// that segment's length; jobs start in order on the first free of `slots`
+// compute units (one workgroup per unit: the LDS ring takes most of it).
+static long long sim_makespan(int cx, int slots, int nb, int na, int nseg, long long L,
+                              long long l0, long long ls)
+{
+    std::vector<long long> free_at((size_t)slots, 0);
+    auto run = [&](long long len) {
+        size_t best = 0;
+        for (size_t i = 1; i < free_at.size(); ++i)
+            if (free_at[i] < free_at[best]) best = i;
+        free_at[best] += len;
+    };
+    for (int j = 0; j < cx * nb; ++j) run(l0 < L ? l0 : L);
+    for (int s = 1; s < nseg; ++s) {
+        long long len = L - l0 - (long long)(s - 1) * ls;
+        len = len < 0 ? 0 : (len < ls ? len : ls);
+        for (int j = 0; j < cx * na; ++j) run(len);
+    }
+    long long m = 0;
+    for (long long f : free_at) m = f > m ? f : m;
+    return m;
+}
+
+// Plans are cached per shape and device size: the search below runs a few
+// hundred list-schedule simulations.
+static std::mutex g_plan_mu;
+static std::map<std::tuple<int, int, int, int, int, int>, SplitPlan> g_plans;
+
+template <int DK, int DV>
+static SplitPlan make_plan(const PrefillArgs &a)
+{
+    SplitPlan pl;
+    if (a.cu_seqlens || DK < 32 || a.n_seqs <= 0 || a.seqlen < 1024) return pl;
+    constexpr int NW = PickNW<DK, DV>::value;
+    constexpr int BV = 16 * NW;
+    constexpr int NB = DV / BV, NA = NB + DK / BV;
+    const int cus = device_cus();
+    const auto key = std::make_tuple(a.n_seqs, a.seqlen, a.H, DK, DV, cus);
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        auto it = g_plans.find(key);
+        if (it != g_plans.end()) return it->second;
+    }
+    const long long chains = (long long)a.n_seqs * a.H;
+    const int slots = cus / 8 > 0 ? cus / 8 : 1;
+    const int cx = (int)((chains + 7) / 8);       // chains on the busiest XCD
+    const long long L = (a.seqlen + 15) / 16;
+    // cost model, in microseconds: a chunk step of a workgroup (measured on
+    // MI355X at d = 128, about 1.25 us whether 128 or 256 units are busy),
+    // and the correction's HBM traffic at 4 TB/s (o~ and R read, o written;
+    // the plan does not depend on the output type) plus two extra launches
+    const double t_chunk = 1.25;
+    auto cost = [&](long long mk, long long aug_tokens) {
+        double c = (double)mk * t_chunk;
+        if (aug_tokens > 0)
+            c += (double)aug_tokens * a.H * (DV * 4 + DK * 4 + DV * 2) / 4.0e6 + 10.0;
+        return c;
+    };
+    double best = cx * NB <= slots ? cost(L, 0) : cost(sim_makespan(cx, slots, NB, NA, 1, L, L, 0), 0);
+    const double base = best;
+    if (cx * NB * 2 <= slots) {   // at most half of an XCD busy: a split can pay
+        for (int nseg = 2; nseg <= 32; ++nseg) {
+            for (int f = 1; f < 40; ++f) {
+                const long long l0 = (L * f + 39) / 40;
+                if (l0 >= L) continue;
+                const long long ls = (L - l0 + nseg - 2) / (nseg - 1);
+                if (ls < 8) continue;
+                const int ns = 1 + (int)((L - l0 + ls - 1) / ls);   // no empty segment
+                const long long mk = sim_makespan(cx, slots, NB, NA, ns, L, l0, ls);
+                const long long aug = (long long)a.n_seqs * (a.seqlen - 16 * l0);
+                const double c = cost(mk, aug);
+                if (c < best) {
+                    best = c;
+                    pl.nseg = ns;
+                    pl.len0 = (int)(16 * l0);
+                    pl.lenS = (int)(16 * ls);
+                }
+            }
+        }
+        if (best > 0.9 * base) pl = SplitPlan{};   // not worth the extra passes
+    }
+    if (pl.nseg > 1) {
+        auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+        const size_t segs = (size_t)chains * (pl.nseg - 1);
+        const size_t aug = (size_t)a.n_seqs * (a.seqlen - pl.len0) * a.H;
+        pl.off_sumst = 0;
+        pl.off_entry = up(segs * DK * (DV + DK) * 4);
+        pl.off_o0 = pl.off_entry + up(segs * DK * DV * 4);
+        pl.off_rq = pl.off_o0 + up(aug * DV * 4);
+        pl.bytes = pl.off_rq + up(aug * DK * 4);
+    }
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_plans[key] = pl;
+    return pl;
+}
+
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
+static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan &pl)
+{
+    using C = Cfg<TI, DK, NW, NBUF>;
+    static_assert(DV % C::BV == 0, "column blocks");
+    constexpr int NB = DV / C::BV, NA = NB + DK / C::BV;
+    const int64_t chains8 = ((chains + 7) / 8) * 8;
+    const int64_t grid = chains8 * (NB + (int64_t)(pl.nseg - 1) * NA);
+    if (grid * C::NT >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // grid size limit
+    Params<TI, TO> p{};
+    p.q = (const TI *)a.q; p.k = (const TI *)a.k; p.v = (const TI *)a.v;
+    p.g = a.g; p.beta = a.beta; p.S0 = a.S0; p.cu_seqlens = a.cu_seqlens;
+    p.o = (TO *)a.o; p.S_T = a.S_T;
+    p.seqlen = a.seqlen; p.n_tokens = (int32_t)a.n_tokens;
+    p.n_chains = (int32_t)chains; p.chains8 = (int32_t)chains8; p.H = a.H;
+    p.nseg = pl.nseg; p.len0 = pl.len0; p.lenS = pl.lenS;
+    if (pl.nseg > 1) {
+        char *ws = static_cast<char *>(a.workspace);
+        p.sumst = reinterpret_cast<float *>(ws + pl.off_sumst);
+        p.entry = reinterpret_cast<float *>(ws + pl.off_entry);
+        p.o0 = reinterpret_cast<float *>(ws + pl.off_o0);
+        p.rq = reinterpret_cast<float *>(ws + pl.off_rq);
+    }
+    hipStream_t st = (hipStream_t)a.stream;
+    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF>), dim3((unsigned)grid),
+                       dim3(C::NT), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || pl.nseg == 1) return e;
+    if (a.S_T || pl.nseg > 2) {
+        hipLaunchKernelGGL((kda_seg_scan_kernel<DK, DV>), dim3((unsigned)(chains * (DV / 16))),
+                           dim3(256), 0, st, p.sumst, p.entry, a.S_T, pl.nseg);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if constexpr (DK % 32 == 0) {
+        const int tiles = (pl.lenS + 255) / 256;
+        const int64_t g2 = chains * (pl.nseg - 1) * tiles;
+        hipLaunchKernelGGL((kda_seg_correct_kernel<TO, DK, DV>), dim3((unsigned)g2), dim3(256), 0,
+                           st, (TO *)a.o, p.o0, p.rq, p.entry, a.H, a.seqlen, pl.len0, pl.lenS,
+                           pl.nseg, tiles);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
 template <typename TI, typename TO, int DK, int DV>
 static hipError_t launch_dims(const PrefillArgs &a)
 {
     constexpr int NW = PickNW<DK, DV>::value;
-    constexpr int NB = DV / (16 * NW);
     const int64_t chains = (int64_t)a.n_seqs * a.H;
     if (chains == 0) return hipSuccess;
     if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
     static_assert(sizeof(Smem<Cfg<TI, DK, NW, 3>>) <= 160 * 1024, "LDS");
-    (void)NB;
-    return launch_t<TI, TO, DK, DV, NW, 3>(a, chains);
+    SplitPlan pl;
+    if (a.workspace) {
+        pl = make_plan<DK, DV>(a);
+        if (pl.bytes > a.workspace_bytes) pl = SplitPlan{};   // (checked by the caller)
+    }
+    return launch_t<TI, TO, DK, DV, NW, 3>(a, chains, pl);
 }
+
+template <int DK, int DV>
+static size_t plan_bytes(const PrefillArgs &a)
+{
+    return make_plan<DK, DV>(a).bytes;
+}
+
+#define KDA_PF_DIMS(X) \
+    X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
+    X(64, 16) X(64, 32) X(64, 64) X(64, 128) X(128, 16) X(128, 32) X(128, 64) X(128, 128)
 
 template <typename TI, typename TO>
 static hipError_t dispatch_dims(const PrefillArgs &a)
 {
 #define KDA_PF_CASE(DK_, DV_) \
     if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_>(a);
-    KDA_PF_CASE(16, 16) KDA_PF_CASE(16, 32) KDA_PF_CASE(16, 64) KDA_PF_CASE(16, 128)
-    KDA_PF_CASE(32, 16) KDA_PF_CASE(32, 32) KDA_PF_CASE(32, 64) KDA_PF_CASE(32, 128)
-    KDA_PF_CASE(64, 16) KDA_PF_CASE(64, 32) KDA_PF_CASE(64, 64) KDA_PF_CASE(64, 128)
-    KDA_PF_CASE(128, 16) KDA_PF_CASE(128, 32) KDA_PF_CASE(128, 64) KDA_PF_CASE(128, 128)
+    KDA_PF_DIMS(KDA_PF_CASE)
 #undef KDA_PF_CASE
     return hipErrorInvalidValue;
+}
+
+size_t prefill_workspace_bytes(const PrefillArgs &a)
+{
+#define KDA_PF_CASE(DK_, DV_) \
+    if (a.d_k == DK_ && a.d_v == DV_) return plan_bytes<DK_, DV_>(a);
+    KDA_PF_DIMS(KDA_PF_CASE)
+#undef KDA_PF_CASE
+    return 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a)

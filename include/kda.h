@@ -47,8 +47,10 @@
  * most recent failure.  Values inside device buffers (cu_seqlens order, the
  * range of g and beta) are preconditions that are NOT checked: g < -5 can
  * overflow the bf16 rescale factors (the 16-token tile bound of the pages
- * assumes g >= -5) and is undefined behaviour; a decreasing cu_seqlens
- * yields unspecified output but stays within the buffers' bounds.
+ * assumes g >= -5) and is undefined behaviour.  The prefill clamps every
+ * cu_seqlens entry into [0, n_tokens] before use, so a cu_seqlens that
+ * breaks its contract (decreasing, negative, or beyond n_tokens) yields
+ * unspecified o and S_T but never an access outside the buffers.
  *
  * Concurrency: calls are asynchronous on `stream` and re-entrant.  Calls
  * that write the same buffers must be ordered by the caller.
@@ -113,14 +115,59 @@ typedef void *kda_stream_t;
  *                      fp32 o is exact fp32 accumulation before any rounding
  *   o                  output (may be NULL iff n_tokens == 0)
  *   S_T                float32 final states or NULL
+ *   workspace          caller-owned device scratch, or NULL
+ *   workspace_bytes    its size; see kda_fwd_workspace_bytes
  *   stream             hipStream_t
+ *
+ * Workspace.  With workspace == NULL and workspace_bytes == 0 the call runs
+ * the single-pass kernel, which needs no scratch.  With a workspace of at
+ * least kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, in_dtype)
+ * bytes (256-byte aligned) the library may instead split long sequences
+ * into segments processed side by side on the device (sequence-split path,
+ * below), which is worthwhile when sequences x heads are too few to fill the
+ * GPU.  A non-NULL workspace that is smaller than that, or misaligned, is
+ * rejected with KDA_ERR_INVALID_ARG.  The contents of the workspace are
+ * undefined after the call; it may not overlap any other argument, and two
+ * calls that are in flight at the same time need separate workspaces.
+ *
+ * Sequence-split path.  Each long sequence is cut into segments.  The first
+ * runs from S0 as usual; every later segment runs from a zero state and, in
+ * the same launch, also carries the d_k columns of its transition matrix
+ * M (the product of its tokens' maps S -> (I - b k k^T) Diag(alpha) S),
+ * which gives the segment's affine summary S_end = M S_entry + S~ and, per
+ * token, the query pulled back to the segment start, R_t = Phi_t^T q_t.  A
+ * scan over segments then gives every segment's true entry state, and a
+ * correction adds R_t S_entry to the zero-start outputs.  This is the
+ * affine-summary-and-prefix-scan scheme the K3-on-TPU essay describes for
+ * context parallelism over KDA (blog.higcp.com, the section on the existing
+ * TPU kernel), used here across compute units of one GPU, which the same
+ * essay names as KDA's intra-device sequence-parallel regime ("KDA + Gated
+ * MLA", the costs section, item (3)).  Results agree with the single-pass
+ * path to rounding.
  */
 kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            const float *g, const float *beta, const float *S0,
                            const int32_t *cu_seqlens, int32_t n_seqs,
                            int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
                            kda_dtype in_dtype, kda_dtype out_dtype, void *o,
-                           float *S_T, kda_stream_t stream);
+                           float *S_T, void *workspace, size_t workspace_bytes,
+                           kda_stream_t stream);
+
+/*
+ * kda_fwd_workspace_bytes -- scratch size for kda_fwd_chunked.
+ *
+ * Returns the number of bytes of workspace with which kda_fwd_chunked, called
+ * with the same sizes on the current device, may take the sequence-split
+ * path; 0 when it would not split (then no workspace is used).  The size
+ * holds the segments' affine summaries and per-token pull-back operands, so
+ * it grows with the number of tokens (at most with the number of chunks)
+ * and never with the state of a longer sequence (the state size does not
+ * depend on T).  For n_seqs > 1 it assumes equal lengths (cu_seqlens ==
+ * NULL); a packed batch of several sequences never uses the workspace.
+ * Invalid sizes give 0 (kda_fwd_chunked then reports the error).
+ */
+size_t kda_fwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                               int32_t d_v, kda_dtype in_dtype);
 
 /*
  * kda_decode_step -- one new token for each of N independent sequences.

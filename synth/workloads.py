@@ -191,15 +191,25 @@ def _threads() -> int:
 
 
 def batch_inputs(wl: Workload, lengths: Optional[np.ndarray] = None,
-                 threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+                 threads: Optional[int] = None,
+                 seqs: Optional[range] = None) -> Dict[str, np.ndarray]:
     """Whole packed batch, token-major, fp32 arrays (bf16-exact for bf16).
 
     Returns q, k [N, H, dk]; v [N, H, dv]; g [N, H, dk]; beta [N, H];
     s0 [n_seqs, H, dk, dv] (only if the workload has a state);
     cu_seqlens int32 [n_seqs + 1]; lengths int64 [n_seqs].
+
+    With `seqs` (a range of sequence indices) only those sequences are
+    generated, packed back to back from token 0 (cu_seqlens local to the
+    group); every value equals the one the whole batch holds for them.
     """
     if lengths is None:
         lengths = seq_lengths(wl)
+    lengths = np.asarray(lengths, np.int64)
+    first = 0
+    if seqs is not None:
+        first = seqs.start
+        lengths = lengths[seqs.start:seqs.stop]
     cu = cu_seqlens(lengths)
     N, H, dk, dv = int(cu[-1]), wl.H, wl.dk, wl.dv
     ns = len(lengths)
@@ -214,7 +224,7 @@ def batch_inputs(wl: Workload, lengths: Optional[np.ndarray] = None,
     def work(nh):
         n, h = nh
         a, b = int(cu[n]), int(cu[n + 1])
-        d = head_inputs(wl, n, h, b - a)
+        d = head_inputs(wl, first + n, h, b - a)
         for key in ("q", "k", "v", "g"):
             out[key][a:b, h] = d[key]
         out["beta"][a:b, h] = d["beta"]

@@ -16,8 +16,8 @@ def lib():
 
 def test_exports_match_header(lib):
     declared = _lib.header_functions()
-    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_last_error",
-                        "kda_status_string", "kda_version"]
+    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_fwd_workspace_bytes",
+                        "kda_last_error", "kda_status_string", "kda_version"]
     for name in declared:
         assert hasattr(lib, name)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -41,11 +41,11 @@ P = 0x10000   # a fake, suitably aligned address: never dereferenced, every
 
 def fwd(lib, **kw):
     a = dict(q=P, k=P * 2, v=P * 3, g=P * 4, beta=P * 5, S0=None, cu=None, n_seqs=1,
-             n_tokens=16, H=1, dk=16, dv=16, ind=1, outd=1, o=P * 6, ST=None)
+             n_tokens=16, H=1, dk=16, dv=16, ind=1, outd=1, o=P * 6, ST=None, ws=None, wsb=0)
     a.update(kw)
     return lib.kda_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["S0"], a["cu"],
                                a["n_seqs"], a["n_tokens"], a["H"], a["dk"], a["dv"], a["ind"],
-                               a["outd"], a["o"], a["ST"], None)
+                               a["outd"], a["o"], a["ST"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -69,6 +69,8 @@ def fwd(lib, **kw):
     (dict(n_tokens=1 << 31, n_seqs=1), 1, "int32"),
     (dict(n_tokens=(1 << 31) - 32, n_seqs=1), 1, "int32"),
     (dict(H=1 << 18, dk=128, dv=128, n_tokens=0, n_seqs=1), 1, "2^25"),
+    (dict(ws=None, wsb=4096), 1, "workspace is NULL"),
+    (dict(ws=P * 8 + 64, wsb=4096), 1, "workspace is not 256-byte aligned"),
 ])
 def test_fwd_validation(lib, kw, status, msg):
     assert fwd(lib, **kw) == status

@@ -1,13 +1,15 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-bench times, on (sequence, head) chains sampled from the whole run.
+bench times, on EVERY (sequence, head) chain of the run.
 
-Each test runs one whole workload through the C ABI, then regenerates the
-sampled chains on the host from the same seeds (synth.head_inputs) and runs
-the fp64 oracle on exactly those chains.  Tolerance as in test_gpu_parity:
-max |x - ref| / rms(ref) <= 2e-2 on o (bf16-stored, half-ulp storage
-allowance) and on S_T.  Every output element is also checked to be finite.
+Each test runs one whole workload through the C ABI into outputs filled with
+NaN beforehand (a chain the kernel skipped cannot pass), then regenerates
+the inputs on the host from the same seeds, group by group, and runs the
+fp64 C oracle on every chain.  Tolerance as in test_gpu_parity: max |x -
+ref| / rms(ref) <= 2e-2 on o (bf16-stored, half-ulp storage allowance) and
+on S_T, with the rms taken over the whole output tensor.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -15,8 +17,8 @@ import torch
 
 from oracle import clib
 from oracle.recurrence import kda_decode_step as ref_decode
-from synth import WORKLOADS, batch_inputs, decode_batch_inputs, head_inputs
-from tests._gpu_util import err, err_bf16_out, to_dev
+from synth import WORKLOADS, batch_inputs, decode_batch_inputs, seq_lengths
+from tests._gpu_util import half_ulp_bf16
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -31,51 +33,137 @@ def kda():
     return m
 
 
-def reference(wl, n, h, T):
-    d = head_inputs(wl, n, h, T)
-    return clib.head(d["q"], d["k"], d["v"], d["g"], d["beta"], d.get("s0"))
+class Acc:
+    """Accumulates max |x - ref| (minus the bf16 storage allowance for o)
+    and sum(ref^2) over groups, so the metric is the whole-tensor one."""
+
+    def __init__(self, bf16_out):
+        self.bf16_out = bf16_out
+        self.max_dev = 0.0
+        self.sq = 0.0
+        self.n = 0
+        self.worst = None
+
+    def add(self, x, ref, tag):
+        x = np.asarray(x, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert x.shape == ref.shape, (x.shape, ref.shape)
+        assert np.all(np.isfinite(x)), f"{tag}: non-finite output (unwritten chain?)"
+        dev = np.abs(x - ref)
+        if self.bf16_out:
+            dev = np.maximum(dev - half_ulp_bf16(ref), 0.0)
+        m = float(np.max(dev, initial=0.0))
+        if m > self.max_dev:
+            self.max_dev, self.worst = m, tag
+        self.sq += float(np.sum(ref * ref))
+        self.n += ref.size
+
+    def error(self):
+        rms = np.sqrt(self.sq / max(self.n, 1))
+        return self.max_dev / rms if rms > 0 else self.max_dev
 
 
-def check_chain(wl, n, h, T, o_gpu, S_gpu, tag, ref=None):
-    o_ref, S_ref = ref if ref is not None else reference(wl, n, h, T)
-    eo, es = err_bf16_out(o_gpu, o_ref), err(S_gpu, S_ref)
-    say(f"  {tag} seq {n} head {h} T {T}: o {eo:.2e}  S_T {es:.2e}")
+def nan_like(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def upload_groups(wl, lengths, groups, shapes):
+    """Generate the packed batch group by group and copy it to the device
+    (bf16 q/k/v, fp32 g/beta); returns device tensors and cu_seqlens."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    N = int(cu[-1])
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    d = {"q": torch.empty((N, H, dk), dtype=dt, device="cuda"),
+         "k": torch.empty((N, H, dk), dtype=dt, device="cuda"),
+         "v": torch.empty((N, H, dv), dtype=dt, device="cuda"),
+         "g": torch.empty((N, H, dk), dtype=torch.float32, device="cuda"),
+         "beta": torch.empty((N, H), dtype=torch.float32, device="cuda")}
+    if wl.s0_sigma is not None:
+        d["s0"] = torch.empty((len(lengths), H, dk, dv), dtype=torch.float32, device="cuda")
+    for g0, g1 in groups:
+        b = batch_inputs(wl, lengths=lengths, seqs=range(g0, g1))
+        a, c = int(cu[g0]), int(cu[g1])
+        for key in ("q", "k", "v", "g", "beta"):
+            d[key][a:c].copy_(torch.from_numpy(b[key]))
+        if "s0" in d:
+            d["s0"][g0:g1].copy_(torch.from_numpy(b["s0"]))
+        del b
+    d["cu_seqlens"] = torch.from_numpy(cu.astype(np.int32)).cuda()
+    return d
+
+
+def seq_groups(lengths, tokens_per_group):
+    groups, g0, acc = [], 0, 0
+    for n, L in enumerate(lengths):
+        acc += int(L)
+        if acc >= tokens_per_group:
+            groups.append((g0, n + 1))
+            g0, acc = n + 1, 0
+    if g0 < len(lengths):
+        groups.append((g0, len(lengths)))
+    return groups
+
+
+def check_packed(wl, lengths, o, S_T, groups, tag):
+    """Every chain of the packed output o [N, H, dv] (host float32, bf16
+    values) and S_T [n_seqs, H, dk, dv] against the oracle."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    ao, aS = Acc(wl.dtype == "bf16"), Acc(False)
+    for g0, g1 in groups:
+        t0 = time.perf_counter()
+        b = batch_inputs(wl, lengths=lengths, seqs=range(g0, g1))
+        o_ref, S_ref, used = clib.fwd(b["q"], b["k"], b["v"], b["g"], b["beta"],
+                                      b["cu_seqlens"], b.get("s0"))
+        del b
+        a, c = int(cu[g0]), int(cu[g1])
+        ao.add(o[a:c], o_ref, f"seqs {g0}..{g1 - 1}")
+        aS.add(S_T[g0:g1], S_ref, f"seqs {g0}..{g1 - 1}")
+        del o_ref, S_ref
+        say(f"  {tag}: seqs {g0}..{g1 - 1} ({c - a} tokens) checked on {used} threads "
+            f"in {time.perf_counter() - t0:.1f}s")
+    eo, es = ao.error(), aS.error()
+    say(f"  {tag}: all {len(lengths)} seqs x {wl.H} heads: o {eo:.2e} (worst {ao.worst}), "
+        f"S_T {es:.2e} (worst {aS.worst})")
     assert eo <= TOL and es <= TOL
 
 
-def test_prefill_workload_sampled():
+@pytest.mark.timeout(600)
+def test_prefill_workload_all_chains():
     """4 x 4096 tokens, H = 32, d = 128, bf16, S0 = 0, equal lengths
-    (cu_seqlens = NULL, [B, T, H, d] layout), exactly as bench.py runs it."""
+    (cu_seqlens = NULL, [B, T, H, d] layout), exactly as bench.py runs it;
+    all 128 (sequence, head) chains."""
     wl = WORKLOADS["prefill"]
     say("prefill workload: generating")
-    b = batch_inputs(wl)
-    B, T, H, D = len(b["lengths"]), wl.seqlen, wl.H, wl.dk
-    d = to_dev(b, torch.bfloat16)
+    L = seq_lengths(wl)
+    d = upload_groups(wl, L, [(0, len(L))], None)
+    B, T, H, D = len(L), wl.seqlen, wl.H, wl.dk
     shp = (B, T, H)
-    o, S_T = kda().kda_fwd_chunked(d["q"].view(*shp, D), d["k"].view(*shp, D),
-                                   d["v"].view(*shp, D), d["g"].view(*shp, D),
-                                   d["beta"].view(*shp))
+    o = nan_like((B, T, H, D), torch.bfloat16)
+    S_T = nan_like((B, H, D, D), torch.float32)
+    kda().kda_fwd_chunked(d["q"].view(*shp, D), d["k"].view(*shp, D), d["v"].view(*shp, D),
+                          d["g"].view(*shp, D), d["beta"].view(*shp), o=o, S_T=S_T)
     torch.cuda.synchronize()
     del d
-    assert o.dtype == torch.bfloat16 and o.shape == (B, T, H, D)
-    o = o.float().cpu().numpy()
+    o = o.float().cpu().numpy().reshape(B * T, H, D)
     S_T = S_T.cpu().numpy()
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S_T))
-    for n, h in [(0, 0), (1, 17), (2, 31), (3, 5)]:
-        check_chain(wl, n, h, T, o[n, :, h], S_T[n, h], "prefill")
+    check_packed(wl, L, o, S_T, [(0, 2), (2, 4)], "prefill")
 
 
-def test_long_prefill_sampled_with_carry_over():
-    """1 x 65,536 tokens, H = 64, d = 128, bf16, S0 ~ N(0, 0.02): whole run,
-    and the same run split in two segments with the first one's S_T handed
-    to the second (the split falls inside a chunk)."""
+@pytest.mark.timeout(900)
+def test_long_prefill_all_heads_with_carry_over():
+    """1 x 65,536 tokens, H = 64, d = 128, bf16, S0 ~ N(0, 0.02): the whole
+    run, and the same run split in two segments with the first one's S_T
+    handed to the second (the split falls inside a chunk); all 64 heads."""
     wl = WORKLOADS["long_prefill"]
     say("long prefill: generating")
-    b = batch_inputs(wl)
+    L = seq_lengths(wl)
     T, H, D = wl.seqlen, wl.H, wl.dk
-    d = to_dev(b, torch.bfloat16)
+    d = upload_groups(wl, L, [(0, 1)], None)
     m = kda()
-    o, S_T = m.kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["s0"])
+    o = nan_like((T, H, D), torch.bfloat16)
+    S_T = nan_like((1, H, D, D), torch.float32)
+    m.kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["s0"], o=o, S_T=S_T)
     T1 = 40_007
     seg = lambda x, a, c: x[a:c].contiguous()                       # noqa: E731
     names = ("q", "k", "v", "g", "beta")
@@ -84,62 +172,90 @@ def test_long_prefill_sampled_with_carry_over():
     torch.cuda.synchronize()
     del d
     o = o.float().cpu().numpy()
-    S_T = S_T[0].cpu().numpy()
+    S_T = S_T.cpu().numpy()
     oc = torch.cat([o1, o2]).float().cpu().numpy()
-    S2 = S2[0].cpu().numpy()
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S_T))
-    for h in (0, 37, 63):
-        ref = reference(wl, 0, h, T)
-        check_chain(wl, 0, h, T, o[:, h], S_T[h], "long", ref)
-        check_chain(wl, 0, h, T, oc[:, h], S2[h], "long, two segments", ref)
-
-
-def test_varlen_sampled():
-    """64 sequences, log-uniform lengths in [128, 32768], H = 32, d = 128,
-    bf16, decay stress on heads 0..15, beta = 1 on 10 % of the tokens, keys
-    repeated inside every tile; packed through cu_seqlens."""
-    wl = WORKLOADS["varlen"]
-    say("varlen: generating")
+    S2 = S2.cpu().numpy()
+    del o1, o2, S1
+    say("long prefill: oracle on all 64 heads, 8 at a time")
     b = batch_inputs(wl)
-    lengths, cu = b["lengths"], b["cu_seqlens"]
-    d = to_dev(b, torch.bfloat16)
-    o, S_T = kda().kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                   cu_seqlens=d["cu_seqlens"])
+    acc = {key: Acc(key.startswith("o")) for key in ("o", "S", "o2", "S2")}
+    for h0 in range(0, H, 8):
+        t0 = time.perf_counter()
+        hs = slice(h0, h0 + 8)
+        o_ref, S_ref, used = clib.fwd(b["q"][:, hs], b["k"][:, hs], b["v"][:, hs],
+                                      b["g"][:, hs], b["beta"][:, hs], b["cu_seqlens"],
+                                      b["s0"][:, hs])
+        acc["o"].add(o[:, hs], o_ref, f"heads {h0}..{h0 + 7}")
+        acc["S"].add(S_T[:, hs], S_ref, f"heads {h0}..{h0 + 7}")
+        acc["o2"].add(oc[:, hs], o_ref, f"heads {h0}..{h0 + 7}")
+        acc["S2"].add(S2[:, hs], S_ref, f"heads {h0}..{h0 + 7}")
+        del o_ref, S_ref
+        say(f"  long: heads {h0}..{h0 + 7} checked on {used} threads in "
+            f"{time.perf_counter() - t0:.1f}s")
+    errs = {key: a.error() for key, a in acc.items()}
+    say(f"  long: whole run o {errs['o']:.2e} S_T {errs['S']:.2e}; two segments "
+        f"o {errs['o2']:.2e} S_T {errs['S2']:.2e}")
+    assert max(errs.values()) <= TOL
+
+
+def _varlen_all(name, timeout_groups_tokens):
+    wl = WORKLOADS[name]
+    L = seq_lengths(wl)
+    groups = seq_groups(L, timeout_groups_tokens)
+    say(f"{name}: {len(L)} seqs, {int(L.sum())} tokens; generating in {len(groups)} groups")
+    d = upload_groups(wl, L, groups, None)
+    N, H, D = int(L.sum()), wl.H, wl.dk
+    o = nan_like((N, H, D), torch.bfloat16)
+    S_T = nan_like((len(L), H, D, D), torch.float32)
+    kda().kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                          cu_seqlens=d["cu_seqlens"], o=o, S_T=S_T)
     torch.cuda.synchronize()
     del d
     o = o.float().cpu().numpy()
     S_T = S_T.cpu().numpy()
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S_T))
-    order = np.argsort(lengths)
-    seqs = [int(order[-1]), int(order[0]), int(order[len(order) // 2]), int(order[len(order) // 4])]
-    for n in seqs:
-        a, c = int(cu[n]), int(cu[n + 1])
-        for h in (0, 15, 16, 31):
-            check_chain(wl, n, h, c - a, o[a:c, h], S_T[n, h], "varlen")
+    check_packed(wl, L, o, S_T, groups, name)
 
 
-def test_decode_workload_sampled():
-    """256 sequences x 64 heads, d = 128, one step in place, bf16 o."""
+@pytest.mark.timeout(900)
+def test_varlen_all_chains():
+    """64 sequences, log-uniform lengths in [128, 32768], H = 32, d = 128,
+    bf16, decay stress on heads 0..15, beta = 1 on 10 % of the tokens, keys
+    repeated inside every tile; packed through cu_seqlens (longest-first
+    dispatch); all 64 x 32 chains."""
+    _varlen_all("varlen", 65536)
+
+
+@pytest.mark.timeout(1200)
+def test_varlen_1m_all_chains():
+    """The 2^20-token variant of the same stress batch (162 sequences: the
+    index-order dispatch above 128 sequences); all 162 x 32 chains."""
+    _varlen_all("varlen_1m", 131072)
+
+
+@pytest.mark.timeout(600)
+def test_decode_workload_all_heads():
+    """256 sequences x 64 heads, d = 128, one step in place, bf16 o; every
+    head of o and of the updated state."""
     wl = WORKLOADS["decode"]
     say("decode workload: generating")
     b = decode_batch_inputs(wl)
     d = {key: torch.from_numpy(b[key]).cuda().to(torch.bfloat16) for key in ("q", "k", "v")}
     d.update({key: torch.from_numpy(b[key]).cuda() for key in ("g", "beta", "S")})
-    o = kda().kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S"])
+    o = nan_like((wl.n_seqs, wl.H, wl.dv), torch.bfloat16)
+    kda().kda_decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S"], o=o)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     S = d["S"].cpu().numpy()
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
-    r = np.random.default_rng(1)
-    pick = [(int(n), int(h)) for n, h in zip(r.integers(0, wl.n_seqs, 256),
-                                              r.integers(0, wl.H, 256))]
-    sel = lambda x: np.stack([x[n, h] for n, h in pick])[:, None]   # noqa: E731
-    o_ref, S_ref = ref_decode(sel(b["q"]), sel(b["k"]), sel(b["v"]), sel(b["g"]),
-                              sel(b["beta"]), sel(b["S"]))
-    eo = err_bf16_out(np.stack([o[n, h] for n, h in pick])[:, None], o_ref)
-    es = err(np.stack([S[n, h] for n, h in pick])[:, None], S_ref)
-    say(f"  decode 256 sampled heads: o {eo:.2e}  S {es:.2e}")
-    assert eo <= TOL and es <= TOL
+    del d
+    ao, aS = Acc(True), Acc(False)
+    for n0 in range(0, wl.n_seqs, 64):
+        ns = slice(n0, n0 + 64)
+        o_ref, S_ref = ref_decode(b["q"][ns], b["k"][ns], b["v"][ns], b["g"][ns],
+                                  b["beta"][ns], b["S"][ns])
+        ao.add(o[ns], o_ref, f"seqs {n0}..{n0 + 63}")
+        aS.add(S[ns], S_ref, f"seqs {n0}..{n0 + 63}")
+    say(f"  decode all {wl.n_seqs} x {wl.H} heads: o {ao.error():.2e}  S {aS.error():.2e}")
+    assert ao.error() <= TOL and aS.error() <= TOL
 
 
 def test_all_sequences_empty():

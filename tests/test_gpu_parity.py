@@ -57,8 +57,10 @@ def test_tiny_fp32_reference_workload():
     assert err(ST, ST_ref) <= 1e-4
 
 
-# the builder's token-group prefix takes 1, 2, 4 or 8 groups depending on
-# d_k / (consumer waves); (128, 32) and (64, 16) give two groups
+# every (d_k, d_v) pair the library builds is covered between the shapes
+# here and the decode tests: narrow value blocks (d_v = 16, 32) with wide
+# keys, and the builder's two token-group layouts (four groups at d_k = 128,
+# eight below)
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128),
                                    (128, 32), (64, 16)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -140,6 +142,43 @@ def test_carry_over_segments():
     assert err(oc, o_ref) <= 2e-2
     assert err(S2.cpu().numpy(), S_ref) <= 2e-2
     assert err(o_full.cpu().numpy(), o_ref) <= 2e-2
+
+
+def test_no_final_state():
+    """S_T == NULL (output_final_state=False): o is still right and no state
+    is written."""
+    b = random_batch(13, [70, 16, 3], H=2, dk=128, dv=128)
+    say("no final state")
+    d = to_dev(b, torch.bfloat16)
+    o, ST = kda().kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=d["s0"],
+                                  cu_seqlens=d["cu_seqlens"], out_dtype=torch.float32,
+                                  output_final_state=False)
+    torch.cuda.synchronize()
+    assert ST is None
+    o_ref, _ = oracle(b)
+    assert err(o.cpu().numpy(), o_ref) <= 2e-2
+
+
+def test_cu_seqlens_out_of_contract_stays_in_bounds():
+    """A cu_seqlens past n_tokens (decreasing, [0, 300, 200] with 200 tokens)
+    is clamped into [0, n_tokens]: nothing is read or written outside the
+    buffers.  o sits at the start of a larger allocation whose tail is a
+    guard that must come back untouched."""
+    H, D, N = 2, 64, 200
+    b = random_batch(17, [N], H=H, dk=D, dv=D)
+    say("cu_seqlens clamp")
+    d = to_dev(b, torch.bfloat16)
+    cu = torch.tensor([0, 300, 200], dtype=torch.int32, device="cuda")
+    S0 = torch.randn(2, H, D, D, device="cuda")
+    big = torch.full((N + 64, H, D), 7.0, dtype=torch.float32, device="cuda")
+    o = big[:N]
+    _, ST = kda().kda_fwd_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], S0=S0,
+                                  cu_seqlens=cu, out_dtype=torch.float32, o=o)
+    torch.cuda.synchronize()
+    assert torch.all(big[N:] == 7.0)
+    assert torch.all(torch.isfinite(o)) and torch.all(torch.isfinite(ST))
+    # after clamping, sequence 1 is empty: its state passes through
+    assert torch.equal(ST[1], S0[1])
 
 
 def test_deterministic():
