@@ -72,7 +72,7 @@ def kda_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                     output_final_state: bool = True,
                     o: Optional[torch.Tensor] = None,
                     S_T: Optional[torch.Tensor] = None,
-                    workspace: Union[None, bool, torch.Tensor] = False,
+                    workspace: Union[None, bool, torch.Tensor] = None,
                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.
 

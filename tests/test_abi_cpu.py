@@ -113,3 +113,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def test_workspace_size_query(lib):
+    """kda_fwd_workspace_bytes: 0 where the chains fill the device (the bench
+    workload) or the batch is empty or invalid; nonzero for one long
+    sequence with few heads."""
+    ws = lib.kda_fwd_workspace_bytes
+    assert ws(4, 4 * 4096, 32, 128, 128, 1) == 0
+    assert ws(0, 0, 8, 128, 128, 1) == 0
+    assert ws(1, 65536, 8, 48, 128, 1) == 0          # unsupported d_k
+    assert ws(1, 65536, 8, 128, 128, 7) == 0         # not a dtype
+    assert ws(1, 65536, 8, 128, 128, 1) > 0
+    assert ws(1, 65536, 8, 128, 128, 1) % 256 == 0
+
+
+def test_workspace_grows_with_chunks_not_state(lib):
+    """Pin p4 on the library: the scratch holds per-token operands and
+    per-segment summaries, so bytes per 16-token chunk stay below a bound
+    that does not depend on T (state size never scales with T)."""
+    H, dk, dv = 8, 128, 128
+    per_chunk_bound = H * (16 * (dk + dv) * 4 + dk * (2 * dv + dk) * 4 // 8) + 4 * 256
+    for T in (1024, 4096, 16384, 65536, 262144, 1 << 20):
+        b = lib.kda_fwd_workspace_bytes(1, T, H, dk, dv, 1)
+        chunks = (T + 15) // 16
+        assert b <= chunks * per_chunk_bound, (T, b)
+
+
+def test_too_small_workspace_rejected(lib):
+    need = lib.kda_fwd_workspace_bytes(1, 65536, 8, 128, 128, 1)
+    assert need > 0
+    st = fwd(lib, n_tokens=65536, H=8, dk=128, dv=128, ws=P * 8, wsb=need - 256)
+    assert st == 1 and "below" in _lib.last_error()
