@@ -258,4 +258,13 @@ KDA_API const char *kda_status_string(kda_status s)
 
 KDA_API const char *kda_last_error(void) { return g_err; }
 
+kda_status kda::set_error(kda_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
 KDA_API const char *kda_version(void) { return "0.1 gfx950"; }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 struct DecodeArgs {
@@ -39,5 +41,8 @@ hipError_t launch_decode(const DecodeArgs &a);
 // fields of `a` (and whether cu_seqlens is set).
 size_t prefill_workspace_bytes(const PrefillArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
+
+// Records a message for kda_last_error() on the calling thread and returns s.
+kda_status set_error(kda_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
 }  // namespace kda

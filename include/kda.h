@@ -170,6 +170,32 @@ size_t kda_fwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H, int3
                                int32_t d_v, kda_dtype in_dtype);
 
 /*
+ * kda_fwd_chunked_noalloc -- kda_fwd_chunked for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, layouts, results and errors as kda_fwd_chunked, without
+ * the workspace pair: where kda_fwd_chunked would use a workspace (the
+ * sequence-split path, kda_fwd_workspace_bytes > 0) this call takes it from
+ * a fixed array of KDA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on, until the process ends; nothing is allocated or freed.
+ * Sizes whose workspace exceeds that are rejected with KDA_ERR_INVALID_ARG
+ * (kda_fwd_chunked with a caller workspace serves them).  Every call on a
+ * device shares that device's array and leaves its contents behind (every
+ * element the split path reads is written earlier in the same call, so
+ * nothing needs clearing): calls that overlap in time on one device, on
+ * different streams or threads, race and must be ordered by the caller.
+ * The array's address on a device is looked up at that device's first call.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t n_seqs,
+                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   float *S_T, kda_stream_t stream);
+
+/*
  * kda_decode_step -- one new token for each of N independent sequences.
  *
  * Applies the recurrence once per (sequence n, head h), updating

@@ -16,8 +16,9 @@ def lib():
 
 def test_exports_match_header(lib):
     declared = _lib.header_functions()
-    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_fwd_workspace_bytes",
-                        "kda_last_error", "kda_status_string", "kda_version"]
+    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_fwd_chunked_noalloc",
+                        "kda_fwd_workspace_bytes", "kda_last_error", "kda_status_string",
+                        "kda_version"]
     for name in declared:
         assert hasattr(lib, name)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -145,3 +146,13 @@ def test_too_small_workspace_rejected(lib):
     assert need > 0
     st = fwd(lib, n_tokens=65536, H=8, dk=128, dv=128, ws=P * 8, wsb=need - 256)
     assert st == 1 and "below" in _lib.last_error()
+
+
+def test_noalloc_rejects_scratch_beyond_its_maximum(lib):
+    """kda_fwd_chunked_noalloc refuses sizes whose split workspace exceeds
+    its fixed array, before touching the device."""
+    need = lib.kda_fwd_workspace_bytes(1, 65536, 64, 128, 128, 1)
+    assert need > 64 << 20
+    st = lib.kda_fwd_chunked_noalloc(P, P * 2, P * 3, P * 4, P * 5, None, None, 1, 65536, 64,
+                                     128, 128, 1, 1, P * 6, None, None)
+    assert st == 1 and "scratch" in _lib.last_error()
