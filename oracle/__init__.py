@@ -20,11 +20,14 @@ Modules
   transition  brute-force product of explicit d_k x d_k transition matrices
   chunked     fp64 chunked (WY/UT) form with 16-token tile re-referencing,
               used to check the chunk algebra before it is trusted on the GPU
+  spec        speculative-decoding verify / replay, as compositions of the
+              recurrence
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against facts that
+Every function is pinned (``tests/test_oracle_pins.py``, ``tests/test_oracle_spec.py``) against facts that
 do not come from the oracle itself (closed forms, a hand-derived example,
 retrieval identities, brute force, invariants); none is "parity unpinned".
 """
 from .recurrence import kda_recurrent, kda_recurrent_varlen, kda_decode_step  # noqa: F401
 from .transition import kda_transition_bruteforce  # noqa: F401
 from .chunked import kda_chunked  # noqa: F401
+from .spec import kda_spec_verify, kda_spec_commit, kda_spec_step  # noqa: F401
