@@ -7,6 +7,9 @@ library's hand-written gfx950 kernels.  Names follow the C ABI:
     kda_fwd_chunked(q, k, v, g, beta, S0=None, cu_seqlens=None, ...) -> (o, S_T)
     kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, dtype) -> int
     kda_decode_step(q, k, v, g, beta, S, ...) -> o        (S updated in place)
+    kda_decode_verify(q, k, v, g, beta, S, ...) -> o      (K drafts, S read only)
+    kda_decode_commit(k, v, g, beta, n_accept, S)         (replay accepted, S in place)
+    kda_decode_spec(q, k, v, g, beta, S, prev, n_accept) -> o   (both in one pass)
 """
 from __future__ import annotations
 
@@ -17,7 +20,8 @@ import torch
 from . import _lib
 from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
 
-__all__ = ["kda_fwd_chunked", "kda_fwd_workspace_bytes", "kda_decode_step", "KDAError",
+__all__ = ["kda_fwd_chunked", "kda_fwd_workspace_bytes", "kda_decode_step",
+           "kda_decode_verify", "kda_decode_commit", "kda_decode_spec", "KDAError",
            "version", "library_path"]
 
 
@@ -166,5 +170,90 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     lib = _lib.load()
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
                              N, H, dk, dv, _dt(q.dtype), _dt(od), _ptr(o), _stream(dev))
+    _lib.check(st)
+    return o
+
+
+def _draft_shapes(q, k, v, g, beta, name="q"):
+    if q.dim() != 4:
+        raise ValueError(f"{name} must be [N, K, H, d_k]")
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _need(q, name, device=dev)
+    _need(k, "k", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(v, "v", dtype=q.dtype, shape=(N, K, H, dv), device=dev)
+    _need(g, "g", dtype=torch.float32, shape=(N, K, H, dk), device=dev)
+    _need(beta, "beta", dtype=torch.float32, shape=(N, K, H), device=dev)
+    return N, K, H, dk, dv
+
+
+def kda_decode_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, S: torch.Tensor,
+                      out_dtype: Optional[torch.dtype] = None,
+                      o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Outputs of K drafted tokens per sequence without committing them.
+    q, k, g : [N, K, H, d_k]; v : [N, K, H, d_v]; beta : [N, K, H];
+    S : [N, H, d_k, d_v] fp32, read only.  Returns o [N, K, H, d_v]."""
+    N, K, H, dk, dv = _draft_shapes(q, k, v, g, beta)
+    dev = q.device
+    _need(S, "S", dtype=torch.float32, shape=(N, H, dk, dv), device=dev)
+    od = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=od, device=dev)
+    else:
+        _need(o, "o", dtype=od, shape=(N, K, H, dv), device=dev)
+    st = _lib.load().kda_decode_verify(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S),
+                                       N, K, H, dk, dv, _dt(q.dtype), _dt(od), _ptr(o),
+                                       _stream(dev))
+    _lib.check(st)
+    return o
+
+
+def kda_decode_commit(k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                      n_accept: torch.Tensor, S: torch.Tensor) -> None:
+    """Replay the first n_accept[n] of the K cached tokens of sequence n into
+    S (in place).  k, g : [N, K, H, d_k]; v : [N, K, H, d_v]; beta :
+    [N, K, H]; n_accept : int32 [N] on the device."""
+    N, K, H, dk, dv = _draft_shapes(k, k, v, g, beta, name="k")
+    dev = k.device
+    _need(S, "S", dtype=torch.float32, shape=(N, H, dk, dv), device=dev)
+    _need(n_accept, "n_accept", dtype=torch.int32, shape=(N,), device=dev)
+    st = _lib.load().kda_decode_commit(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(n_accept),
+                                       _ptr(S), N, K, H, dk, dv, _dt(k.dtype), _stream(dev))
+    _lib.check(st)
+
+
+def kda_decode_spec(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor, prev: Optional[dict] = None,
+                    n_accept: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None,
+                    o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One speculative decode step: commit prev's accepted drafts (a dict of
+    k, v, g, beta shaped [N, K_prev, H, ...], n_accept int32 [N]) into S,
+    then verify the new drafts q, k, v, g, beta [N, K, H, ...] from it.
+    Returns o [N, K, H, d_v]; S is updated in place."""
+    N, K, H, dk, dv = _draft_shapes(q, k, v, g, beta)
+    dev = q.device
+    _need(S, "S", dtype=torch.float32, shape=(N, H, dk, dv), device=dev)
+    Kp = 0
+    pk = pv = pg = pb = None
+    if prev is not None:
+        pk, pv, pg, pb = prev["k"], prev["v"], prev["g"], prev["beta"]
+        Np, Kp, Hp, dkp, dvp = _draft_shapes(pk, pk, pv, pg, pb, name="prev k")
+        if (Np, Hp, dkp, dvp) != (N, H, dk, dv) or pk.dtype != q.dtype:
+            raise ValueError("prev drafts must match the new drafts in N, H, d and dtype")
+        if n_accept is None:
+            raise ValueError("n_accept is required with prev")
+        _need(n_accept, "n_accept", dtype=torch.int32, shape=(N,), device=dev)
+    od = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, K, H, dv), dtype=od, device=dev)
+    else:
+        _need(o, "o", dtype=od, shape=(N, K, H, dv), device=dev)
+    st = _lib.load().kda_decode_spec(_ptr(pk), _ptr(pv), _ptr(pg), _ptr(pb),
+                                     _ptr(n_accept) if prev is not None else None, Kp,
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), K, _ptr(S),
+                                     N, H, dk, dv, _dt(q.dtype), _dt(od), _ptr(o), _stream(dev))
     _lib.check(st)
     return o

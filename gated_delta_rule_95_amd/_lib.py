@@ -53,6 +53,15 @@ def load() -> ctypes.CDLL:
         lib.kda_decode_step.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32,
                                         ctypes.c_int, ctypes.c_int, P, P]
+        lib.kda_decode_verify.restype = ctypes.c_int
+        lib.kda_decode_verify.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                          ctypes.c_int, ctypes.c_int, P, P]
+        lib.kda_decode_commit.restype = ctypes.c_int
+        lib.kda_decode_commit.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                          ctypes.c_int, P]
+        lib.kda_decode_spec.restype = ctypes.c_int
+        lib.kda_decode_spec.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32,
+                                        I32, I32, ctypes.c_int, ctypes.c_int, P, P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p

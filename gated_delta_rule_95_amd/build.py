@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_noalloc.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_noalloc.hip",
+           "kda_spec.hip"]
 
 
 def hipcc() -> str:

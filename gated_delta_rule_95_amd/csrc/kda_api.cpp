@@ -245,6 +245,146 @@ KDA_API kda_status kda_decode_step(const void *q, const void *k, const void *v,
     return hip_status(kda::launch_decode(a), "kda_decode_step launch");
 }
 
+namespace {
+
+// Shared validation of the speculative-decoding calls.  Token tensors are
+// [N, K, H, d] (one row of K tokens per sequence), the state [N, H, d_k, d_v].
+kda_status check_spec(const char *fn, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                      int32_t K, int32_t K_min, const char *kname)
+{
+    kda_status s;
+    if ((s = check_dims(H, d_k, d_v)) != KDA_OK) return s;
+    if (N < 0) return fail(KDA_ERR_INVALID_ARG, "%s: N must be >= 0 (got %d)", fn, N);
+    if (K < K_min || K > kda::kSpecMaxTokens)
+        return fail(KDA_ERR_INVALID_ARG, "%s: %s must be in [%d, %d] (got %d)", fn, kname, K_min,
+                    kda::kSpecMaxTokens, K);
+    return KDA_OK;
+}
+
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+
+// true if one of the first nw spans (the written ones) overlaps any other
+// span of the na
+bool spans_overlap(const Span *all, int nw, int na)
+{
+    for (int i = 0; i < nw; ++i)
+        for (int j = 0; j < na; ++j)
+            if (j != i && overlap(all[i].p, all[i].bytes, all[j].p, all[j].bytes))
+                return true;
+    return false;
+}
+
+kda_status run_spec(kda::SpecArgs &a, const char *fn)
+{
+    return hip_status(kda::launch_spec(a), fn);
+}
+
+}  // namespace
+
+KDA_API kda_status kda_decode_verify(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta, const float *S,
+                                     int32_t N, int32_t K, int32_t H, int32_t d_k, int32_t d_v,
+                                     kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                     kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
+    if ((s = check_spec("kda_decode_verify", N, H, d_k, d_v, K, 1, "K")) != KDA_OK) return s;
+    if (N == 0) return ok();
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
+    const Ptr ps[] = {{q, "q", true, in_b}, {k, "k", true, in_b}, {v, "v", true, 4 * in_b},
+                      {g, "g", true, 4}, {beta, "beta", true, 4}, {S, "S", true, 16},
+                      {o, "o", true, 4 * out_b}};
+    if ((s = check_ptrs(ps, 7)) != KDA_OK) return s;
+    const size_t nt = (size_t)N * K * H;
+    const Span all[] = {{o, nt * d_v * out_b}, {q, nt * d_k * in_b}, {k, nt * d_k * in_b},
+                        {v, nt * d_v * in_b}, {g, nt * d_k * 4}, {beta, nt * 4},
+                        {S, (size_t)N * H * d_k * d_v * 4}};
+    if (spans_overlap(all, 1, 7))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_verify: o overlaps an input");
+    kda::SpecArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.K = K;
+    a.S = const_cast<float *>(S);         // read only: write_state is false
+    a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.write_state = false; a.stream = stream;
+    return run_spec(a, "kda_decode_verify launch");
+}
+
+KDA_API kda_status kda_decode_commit(const void *k, const void *v, const float *g,
+                                     const float *beta, const int32_t *n_accept, float *S,
+                                     int32_t N, int32_t K, int32_t H, int32_t d_k, int32_t d_v,
+                                     kda_dtype in_dtype, kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, in_dtype)) != KDA_OK) return s;
+    if ((s = check_spec("kda_decode_commit", N, H, d_k, d_v, K, 0, "K")) != KDA_OK) return s;
+    if (N == 0 || K == 0) return ok();
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4;
+    const Ptr ps[] = {{k, "k", true, in_b}, {v, "v", true, 4 * in_b}, {g, "g", true, 4},
+                      {beta, "beta", true, 4}, {n_accept, "n_accept", true, 4},
+                      {S, "S", true, 16}};
+    if ((s = check_ptrs(ps, 6)) != KDA_OK) return s;
+    const size_t nt = (size_t)N * K * H;
+    const Span all[] = {{S, (size_t)N * H * d_k * d_v * 4}, {k, nt * d_k * in_b},
+                        {v, nt * d_v * in_b}, {g, nt * d_k * 4}, {beta, nt * 4},
+                        {n_accept, (size_t)N * 4}};
+    if (spans_overlap(all, 1, 6))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_commit: S overlaps another argument");
+    kda::SpecArgs a{};
+    a.rk = k; a.rv = v; a.rg = g; a.rbeta = beta; a.n_accept = n_accept; a.Kr = K;
+    a.K = 0; a.S = S; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = a.in_bf16;
+    a.write_state = true; a.stream = stream;
+    return run_spec(a, "kda_decode_commit launch");
+}
+
+KDA_API kda_status kda_decode_spec(const void *k_prev, const void *v_prev, const float *g_prev,
+                                   const float *beta_prev, const int32_t *n_accept,
+                                   int32_t K_prev, const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, int32_t K, float *S,
+                                   int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
+    if ((s = check_spec("kda_decode_spec", N, H, d_k, d_v, K, 1, "K")) != KDA_OK) return s;
+    if (K_prev < 0 || K_prev > kda::kSpecMaxTokens)
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_spec: K_prev must be in [0, %d] (got %d)",
+                    kda::kSpecMaxTokens, K_prev);
+    if (N == 0) return ok();
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
+    const bool prev = K_prev > 0;
+    const Ptr ps[] = {{q, "q", true, in_b}, {k, "k", true, in_b}, {v, "v", true, 4 * in_b},
+                      {g, "g", true, 4}, {beta, "beta", true, 4}, {S, "S", true, 16},
+                      {o, "o", true, 4 * out_b}, {k_prev, "k_prev", prev, in_b},
+                      {v_prev, "v_prev", prev, 4 * in_b}, {g_prev, "g_prev", prev, 4},
+                      {beta_prev, "beta_prev", prev, 4}, {n_accept, "n_accept", prev, 4}};
+    if ((s = check_ptrs(ps, 12)) != KDA_OK) return s;
+    const size_t nt = (size_t)N * K * H, np = (size_t)N * K_prev * H;
+    const Span all[] = {{S, (size_t)N * H * d_k * d_v * 4}, {o, nt * d_v * out_b},
+                        {q, nt * d_k * in_b}, {k, nt * d_k * in_b}, {v, nt * d_v * in_b},
+                        {g, nt * d_k * 4}, {beta, nt * 4}, {k_prev, np * d_k * in_b},
+                        {v_prev, np * d_v * in_b}, {g_prev, np * d_k * 4}, {beta_prev, np * 4},
+                        {n_accept, prev ? (size_t)N * 4 : 0}};
+    if (spans_overlap(all, 2, 12))
+        return fail(KDA_ERR_INVALID_ARG, "kda_decode_spec: S or o overlaps another argument");
+    kda::SpecArgs a{};
+    if (prev) {
+        a.rk = k_prev; a.rv = v_prev; a.rg = g_prev; a.rbeta = beta_prev;
+        a.n_accept = n_accept; a.Kr = K_prev;
+    }
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.K = K;
+    a.S = S; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = out_dtype == KDA_BF16;
+    a.write_state = true; a.stream = stream;
+    return run_spec(a, "kda_decode_spec launch");
+}
+
 KDA_API const char *kda_status_string(kda_status s)
 {
     switch (s) {

@@ -35,7 +35,27 @@ struct PrefillArgs {
     void *stream;
 };
 
+// Speculative decoding (kda_decode_verify / _commit / _spec): replay up to
+// Kr cached tokens per sequence (n_accept[n] of them) into S, optionally
+// write S, then run K drafts from the result and write their outputs.
+constexpr int kSpecMaxTokens = 16;
+struct SpecArgs {
+    const void *rk, *rv;             // [N, Kr, H, d] replayed tokens
+    const float *rg, *rbeta;
+    const int32_t *n_accept;         // [N] or nullptr (nothing replayed)
+    int32_t Kr;
+    const void *q, *k, *v;           // [N, K, H, d] drafts
+    const float *g, *beta;
+    void *o;                         // [N, K, H, d_v]
+    int32_t K;
+    float *S;
+    int32_t N, H, d_k, d_v;
+    bool in_bf16, out_bf16, write_state;
+    void *stream;
+};
+
 hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_spec(const SpecArgs &a);
 // Bytes of workspace the sequence-split path needs for these sizes on the
 // current device (0: the single-pass kernel is used).  Reads only the size
 // fields of `a` (and whether cu_seqlens is set).

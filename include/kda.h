@@ -220,6 +220,52 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            kda_dtype in_dtype, kda_dtype out_dtype, void *o,
                            kda_stream_t stream);
 
+/*
+ * Speculative decoding: verify drafted tokens, replay the accepted ones.
+ *
+ * The decode step updates the state in place, so once a draft is rejected
+ * the state cannot be rolled back, and keeping a state snapshot per draft
+ * position multiplies the state traffic that dominates large-batch serving.
+ * The pages describe K3 keeping only each draft's inputs and replaying the
+ * accepted ones on chip to rebuild the state (K3-on-TPU essay,
+ * blog.higcp.com, "KDA + Gated MLA", the costs section, item (1)).  These
+ * calls do that for the KDA recurrence; the drafts' inputs are the caller's
+ * (the cache of "projected inputs").
+ *
+ * Token tensors hold K tokens per sequence, token-major within a sequence:
+ *     q, k, g  [N, K, H, d_k]    v, o  [N, K, H, d_v]    beta  [N, K, H]
+ * (dtypes as for kda_decode_step); S is [N, H, d_k, d_v] float32; n_accept
+ * is int32 [N] in device memory, each entry clamped into [0, K] (an entry
+ * out of range changes the result, never the addresses touched).
+ * 1 <= K <= 16 for drafts (0 <= K <= 16 for kda_decode_commit).  Alignment
+ * as for kda_decode_step.  Errors as for the other entry points.
+ *
+ * kda_decode_verify  runs the K drafts of every sequence from S and writes
+ *     o for each draft position (o[n, j] is what decoding drafts 0..j one at
+ *     a time would output).  S is read only.
+ * kda_decode_commit  replays the first n_accept[n] tokens of sequence n
+ *     into S[n] (in place), as that many kda_decode_step calls would.
+ * kda_decode_spec    one pass of both, for a decode loop: first commits the
+ *     previous step's drafts (k_prev ... beta_prev, K_prev per sequence,
+ *     n_accept[n] of them accepted; K_prev = 0 and NULL pointers for none)
+ *     into S, then verifies the K new drafts from the updated S.  The state
+ *     is read once and written once, the traffic of one decode step.
+ */
+kda_status kda_decode_verify(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *S, int32_t N, int32_t K,
+                             int32_t H, int32_t d_k, int32_t d_v, kda_dtype in_dtype,
+                             kda_dtype out_dtype, void *o, kda_stream_t stream);
+kda_status kda_decode_commit(const void *k, const void *v, const float *g, const float *beta,
+                             const int32_t *n_accept, float *S, int32_t N, int32_t K,
+                             int32_t H, int32_t d_k, int32_t d_v, kda_dtype in_dtype,
+                             kda_stream_t stream);
+kda_status kda_decode_spec(const void *k_prev, const void *v_prev, const float *g_prev,
+                           const float *beta_prev, const int32_t *n_accept, int32_t K_prev,
+                           const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, int32_t K, float *S, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                           void *o, kda_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *kda_status_string(kda_status s);
 

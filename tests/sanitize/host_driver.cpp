@@ -23,7 +23,8 @@ void kda_oracle_head(int64_t T, int dk, int dv, const float *q, const float *k,
 }
 
 namespace kda {
-static int g_prefill_calls = 0, g_decode_calls = 0;
+static int g_prefill_calls = 0, g_decode_calls = 0, g_spec_calls = 0;
+static SpecArgs g_last_spec;
 static PrefillArgs g_last_prefill;
 size_t prefill_workspace_bytes(const PrefillArgs &a)
 {
@@ -39,6 +40,12 @@ hipError_t launch_prefill(const PrefillArgs &a)
 hipError_t launch_decode(const DecodeArgs &)
 {
     ++g_decode_calls;
+    return hipSuccess;
+}
+hipError_t launch_spec(const SpecArgs &a)
+{
+    ++g_spec_calls;
+    g_last_spec = a;
     return hipSuccess;
 }
 }  // namespace kda
@@ -115,6 +122,27 @@ int main()
     EXPECT(kda_decode_step(q.data(), k.data(), v.data(), g.data(), beta.data(),
                            reinterpret_cast<float *>(q.data()), 1, 1, 16, 16, KDA_BF16, KDA_BF16,
                            o.data(), nullptr) == KDA_ERR_INVALID_ARG);      // S overlaps q
+    // speculative decoding: [N = 2, K = 4, H, D] drafts fit in the token buffers
+    std::vector<int32_t> acc(2, 3);
+    EXPECT(kda_decode_verify(q.data(), k.data(), v.data(), g.data(), beta.data(), S.data(), 2, 4,
+                             H, D, D, KDA_BF16, KDA_BF16, o.data(), nullptr) == KDA_OK);
+    EXPECT(kda::g_last_spec.write_state == false && kda::g_last_spec.K == 4);
+    EXPECT(kda_decode_commit(k.data(), v.data(), g.data(), beta.data(), acc.data(), S.data(), 2,
+                             4, H, D, D, KDA_BF16, nullptr) == KDA_OK);
+    EXPECT(kda::g_last_spec.write_state && kda::g_last_spec.K == 0 && kda::g_last_spec.Kr == 4);
+    EXPECT(kda_decode_spec(k.data(), v.data(), g.data(), beta.data(), acc.data(), 4, q.data(),
+                           k.data(), v.data(), g.data(), beta.data(), 4, S.data(), 2, H, D, D,
+                           KDA_BF16, KDA_BF16, o.data(), nullptr) == KDA_OK);
+    EXPECT(kda::g_spec_calls == 3);
+    EXPECT(kda_decode_verify(q.data(), k.data(), v.data(), g.data(), beta.data(), S.data(), 2,
+                             17, H, D, D, KDA_BF16, KDA_BF16, o.data(), nullptr) ==
+           KDA_ERR_INVALID_ARG);
+    EXPECT(kda_decode_verify(q.data(), k.data(), v.data(), g.data(), beta.data(), S.data(), 2, 4,
+                             H, D, D, KDA_BF16, KDA_BF16, q.data(), nullptr) ==
+           KDA_ERR_INVALID_ARG);                                          // o overlaps q
+    EXPECT(kda_decode_commit(k.data(), v.data(), g.data(), beta.data(), nullptr, S.data(), 2, 4,
+                             H, D, D, KDA_BF16, nullptr) == KDA_ERR_INVALID_ARG);
+    EXPECT(kda::g_spec_calls == 3);
     EXPECT(std::strcmp(kda_status_string(KDA_ERR_HIP), "KDA_ERR_HIP") == 0);
     EXPECT(std::strcmp(kda_status_string((kda_status)42), "KDA_ERR_UNKNOWN") == 0);
     EXPECT(std::strstr(kda_version(), "gfx950") != nullptr);

@@ -16,7 +16,8 @@ def lib():
 
 def test_exports_match_header(lib):
     declared = _lib.header_functions()
-    assert declared == ["kda_decode_step", "kda_fwd_chunked", "kda_fwd_chunked_noalloc",
+    assert declared == ["kda_decode_commit", "kda_decode_spec", "kda_decode_step",
+                        "kda_decode_verify", "kda_fwd_chunked", "kda_fwd_chunked_noalloc",
                         "kda_fwd_workspace_bytes", "kda_last_error", "kda_status_string",
                         "kda_version"]
     for name in declared:
@@ -156,3 +157,29 @@ def test_noalloc_rejects_scratch_beyond_its_maximum(lib):
     st = lib.kda_fwd_chunked_noalloc(P, P * 2, P * 3, P * 4, P * 5, None, None, 1, 65536, 64,
                                      128, 128, 1, 1, P * 6, None, None)
     assert st == 1 and "scratch" in _lib.last_error()
+
+
+def test_spec_validation(lib):
+    ver, com, spec = lib.kda_decode_verify, lib.kda_decode_commit, lib.kda_decode_spec
+    # verify: K out of range, S misaligned, o overlapping an input
+    assert ver(P, P * 2, P * 3, P * 4, P * 5, P * 64, 2, 0, 1, 16, 16, 1, 1, P * 7, None) == 1
+    assert "K must be in [1, 16]" in _lib.last_error()
+    assert ver(P, P * 2, P * 3, P * 4, P * 5, P * 64, 2, 17, 1, 16, 16, 1, 1, P * 7, None) == 1
+    assert ver(P, P * 2, P * 3, P * 4, P * 5, P * 64 + 8, 2, 4, 1, 16, 16, 1, 1, P * 7,
+               None) == 1 and "aligned" in _lib.last_error()
+    assert ver(P, P * 2, P * 3, P * 4, P * 5, P * 64, 2, 4, 1, 16, 16, 1, 1, P, None) == 1
+    assert "overlaps" in _lib.last_error()
+    assert ver(P, P * 2, P * 3, P * 4, P * 5, P * 64, 0, 4, 1, 16, 16, 1, 1, P * 7, None) == 0
+    # commit: n_accept required, K = 0 is a no-op, S overlapping
+    assert com(P, P * 3, P * 4, P * 5, None, P * 64, 2, 3, 1, 16, 16, 1, None) == 1
+    assert "n_accept is NULL" in _lib.last_error()
+    assert com(P, P * 3, P * 4, P * 5, None, P * 64, 2, 0, 1, 16, 16, 1, None) == 0
+    assert com(P, P * 3, P * 4, P * 5, P * 6, P, 2, 3, 1, 16, 16, 1, None) == 1
+    assert "S overlaps" in _lib.last_error()
+    # spec: K_prev out of range; previous drafts required when K_prev > 0
+    assert spec(None, None, None, None, None, 17, P, P * 2, P * 3, P * 4, P * 5, 2, P * 64,
+                1, 1, 16, 16, 1, 1, P * 7, None) == 1
+    assert "K_prev" in _lib.last_error()
+    assert spec(None, None, None, None, None, 2, P, P * 2, P * 3, P * 4, P * 5, 2, P * 64,
+                1, 1, 16, 16, 1, 1, P * 7, None) == 1
+    assert "k_prev is NULL" in _lib.last_error()
