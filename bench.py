@@ -27,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+SPEC_K = 4                       # drafts per speculative step (previous and new)
+SEED_ACCEPT = 0x4B4441 + 17      # seeded acceptance counts of the speculative leg
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix, published
 PROFILE_PMC = os.path.join(ROOT, "profiles", "kda_prefill_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_95_amd", "csrc", f)
@@ -58,6 +60,16 @@ def decode_bytes(N: int, H: int, dk: int, dv: int) -> tuple:
     return state, state + other
 
 
+def spec_bytes(N: int, H: int, dk: int, dv: int, K: int, K_prev: int) -> tuple:
+    """One fused speculative step: the state read and written once; per
+    previous draft k, v (bf16), g, beta; per new draft q, k, v (bf16), g,
+    beta and o (bf16); the accepted counts."""
+    state = N * H * dk * dv * 4 * 2
+    prev = N * K_prev * H * (2 * dk + 2 * dv + 4 * dk + 4)
+    new = N * K * H * (2 * dk * 2 + 2 * dv + 4 * dk + 4 + 2 * dv)
+    return state, state + prev + new + 4 * N
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -82,9 +94,29 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """What the host offers the oracle: logical CPUs, the CPUs this process
+    may run on, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"nproc": os.cpu_count() or 1, "usable": usable, "model": model}
+
+
 def cpu_baseline(threads: int):
     """The fp64 C oracle on the whole prefill workload (4 sequences x 4096
-    tokens x 32 heads, d = 128; about 20 core-seconds), timed on the host."""
+    tokens x 32 heads, d = 128; about 20 core-seconds) on `threads` host
+    threads, and on one thread over 4 of its 128 (sequence, head) chains."""
     from oracle import clib
     from synth import WORKLOADS, batch_inputs
     wl = WORKLOADS["prefill"]
@@ -94,10 +126,23 @@ def cpu_baseline(threads: int):
     _, _, used = clib.fwd(b["q"], b["k"], b["v"], b["g"], b["beta"], b["cu_seqlens"], None,
                           want_o=True, threads=threads)
     dt = time.perf_counter() - t0
+    # one thread, heads 0..3 of sequence 0 (4 chains of 4096 tokens): tokens/s
+    # scaled to all 32 heads, the unit of the whole-workload figure
+    one = {key: b[key][:wl.seqlen, :4] for key in ("q", "k", "v", "g", "beta")}
+    t1 = time.perf_counter()
+    clib.fwd(one["q"], one["k"], one["v"], one["g"], one["beta"],
+             [0, wl.seqlen], None, want_o=True, threads=1)
+    dt1 = time.perf_counter() - t1
+    one_core = wl.seqlen * 4 / wl.H / dt1
+    host = host_cpu()
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "one_core_value": one_core, "host": host,
             "sample": f"fp64 C oracle (token-by-token, OpenMP over (sequence, head)) on the "
                       f"whole prefill workload: {len(b['lengths'])} seqs x {wl.seqlen} tokens x "
-                      f"{wl.H} heads, d=128; {dt:.2f} s wall on {used} threads"}
+                      f"{wl.H} heads, d=128; {dt:.2f} s wall on {used} threads "
+                      f"({host['usable']} usable of {host['nproc']} logical CPUs, "
+                      f"{host['model']}); one thread: 4 chains of 4096 tokens in {dt1:.2f} s, "
+                      f"scaled to 32 heads"}
 
 
 def main():
@@ -109,6 +154,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "long_prefill", "varlen", "varlen_1m"])
+    ap.add_argument("--heads", type=int, default=0,
+                    help="override the workload's head count (split-threshold study)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="prefill without a workspace: the single-pass kernel only")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -135,6 +184,9 @@ def main():
 
     # ---------------- inputs (generated on the host, seeded) ----------------
     wl = WORKLOADS[args.workload]
+    if args.heads:
+        import dataclasses
+        wl = dataclasses.replace(wl, H=args.heads)
     t0 = time.perf_counter()
     b = batch_inputs(wl)
     log(f"[bench] generated {args.workload}: {int(b['cu_seqlens'][-1])} tokens, "
@@ -153,10 +205,15 @@ def main():
     o = torch.empty(P["v"].shape, dtype=dt_in, device=dev)
     S_T = torch.empty((n_seqs, wl.H, wl.dk, wl.dv), dtype=torch.float32, device=dev)
     del b
+    # the workspace of the sequence-split path is allocated once, outside the
+    # timed region (the library itself allocates nothing)
+    ws_bytes = 0 if (args.no_split or not equal) else \
+        kda.kda_fwd_workspace_bytes(n_seqs, tokens, wl.H, wl.dk, wl.dv, dt_in)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else False
 
     def run_prefill():
         kda.kda_fwd_chunked(P["q"], P["k"], P["v"], P["g"], P["beta"], S0=S0, cu_seqlens=cu,
-                            o=o, S_T=S_T)
+                            o=o, S_T=S_T, workspace=ws)
 
     dec = None
     if not args.no_decode:
@@ -170,6 +227,29 @@ def main():
     def run_decode():
         kda.kda_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], dec["S"],
                             o=dec["o"])
+
+    # speculative step at the decode workload's shape: the previous step's
+    # SPEC_K drafts (a seeded number of them accepted per sequence) are
+    # committed and SPEC_K new drafts verified, in one pass over the state
+    spec = None
+    if dec:
+        from synth import draft_batch_inputs
+        dw = WORKLOADS["decode"]
+        nd, pd = draft_batch_inputs(dw, SPEC_K, 1), draft_batch_inputs(dw, SPEC_K, 2)
+        tod = lambda x, key: (torch.from_numpy(x[key]).to(dev).to(torch.bfloat16)   # noqa
+                              if key in ("q", "k", "v") else torch.from_numpy(x[key]).to(dev))
+        spec = {"new": {key: tod(nd, key) for key in nd}, "prev": {key: tod(pd, key) for key in pd},
+                "acc": torch.from_numpy(np.random.default_rng(SEED_ACCEPT).integers(
+                    0, SPEC_K + 1, dw.n_seqs).astype(np.int32)).to(dev),
+                "S": dec["S"].clone(),
+                "o": torch.empty((dw.n_seqs, SPEC_K, dw.H, dw.dv), dtype=torch.bfloat16,
+                                 device=dev)}
+        del nd, pd
+
+    def run_spec():
+        n = spec["new"]
+        kda.kda_decode_spec(n["q"], n["k"], n["v"], n["g"], n["beta"], spec["S"],
+                            prev=spec["prev"], n_accept=spec["acc"], o=spec["o"])
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -185,12 +265,13 @@ def main():
         run_prefill()
         if dec:
             run_decode()
+            run_spec()
     torch.cuda.synchronize(dev)
     log(f"[bench] warmup {args.warmup} done")
 
     # ---------------- timed steps ----------------
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     for i in range(K):
@@ -201,10 +282,14 @@ def main():
             ev[i][2].record(stream)
             run_decode()
             ev[i][3].record(stream)
+            ev[i][4].record(stream)
+            run_spec()
+            ev[i][5].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
     pf_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
     dc_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) if dec else None
+    sp_ms = np.array([ev[i][4].elapsed_time(ev[i][5]) for i in range(K)]) if dec else None
     log(f"[bench] prefill ms: mean {pf_ms.mean():.4f} min {pf_ms.min():.4f} "
         f"max {pf_ms.max():.4f}")
 
@@ -231,7 +316,7 @@ def main():
                                f"d_k=d_v={wl.dk}, bf16 q/k/v/o, fp32 g/beta/state, "
                                f"S0={'given' if S0 is not None else 'zero'}, S_T returned",
                    "tokens": tokens, "n_seqs": n_seqs, "H": wl.H, "d_k": wl.dk, "d_v": wl.dv,
-                   "chunk": 16,
+                   "chunk": 16, "split_workspace_bytes": int(ws_bytes),
                    "decode_workload": "256 seqs x 64 heads, d=128, fp32 state in place"
                    if dec else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -253,6 +338,16 @@ def main():
                                       "frac": all_b / dc_s / 1e9 / HBM_PEAK_GBS,
                                       "kernel": "kda_decode_kernel",
                                       "alg_bytes_per_launch": all_b}}
+        sst_b, sall_b = spec_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv, SPEC_K, SPEC_K)
+        sp_s = float(sp_ms.mean()) / 1e3
+        out["spec_decode"] = {
+            "workload": f"{dw.n_seqs} seqs x {dw.H} heads, d=128: commit of {SPEC_K} previous "
+                        f"drafts (seeded acceptance 0..{SPEC_K}) + verify of {SPEC_K} new drafts",
+            "launch_ms": sp_s * 1e3, "state_GBps": sst_b / sp_s / 1e9,
+            "draft_tokens_per_s": dw.n_seqs * SPEC_K / sp_s,
+            "roofline": {"bound": "hbm", "achieved": sall_b / sp_s / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": sall_b / sp_s / 1e9 / HBM_PEAK_GBS,
+                         "kernel": "kda_spec_kernel", "alg_bytes_per_launch": sall_b}}
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(threads)

@@ -1148,25 +1148,33 @@ __global__ __launch_bounds__(256) void kda_seg_scan_kernel(const float *__restri
 {
     constexpr int NCB = DV / 16;
     constexpr int PER = (DK * 16 + 255) / 256;   // state elements per thread
+    // M_s staged per step with coalesced row reads; E the running entry
+    // state of this block of 16 columns
+    __shared__ float M[DK][DK + 1];
     __shared__ float E[DK][17];
     const int chain = blockIdx.x / NCB, cb = blockIdx.x % NCB;
     const int tid = threadIdx.x;
     const int64_t ebase = (int64_t)chain * (nseg - 1) * DK * DV + cb * 16;
     for (int e = tid; e < DK * 16; e += 256) E[e / 16][e % 16] = entry[ebase + (e / 16) * DV + e % 16];
-    __syncthreads();
     for (int s = 1; s < nseg; ++s) {
         const float *A = sumst + ((int64_t)chain * (nseg - 1) + s - 1) * DK * (DV + DK);
+        for (int e = tid; e < DK * DK; e += 256)
+            M[e / DK][e % DK] = A[(int64_t)(e / DK) * (DV + DK) + DV + e % DK];
         float acc[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = tid + 256 * i;
-            acc[i] = 0.f;
+            acc[i] = e < DK * 16 ? A[(int64_t)(e / 16) * (DV + DK) + cb * 16 + e % 16] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + 256 * i;
             if (e < DK * 16) {
                 const int r = e / 16, c = e % 16;
-                const float *Ar = A + (int64_t)r * (DV + DK);
-                float a = Ar[cb * 16 + c];
+                float a = acc[i];
 #pragma unroll 8
-                for (int kk = 0; kk < DK; ++kk) a = __builtin_fmaf(Ar[DV + kk], E[kk][c], a);
+                for (int kk = 0; kk < DK; ++kk) a = __builtin_fmaf(M[r][kk], E[kk][c], a);
                 acc[i] = a;
             }
         }
@@ -1181,7 +1189,7 @@ __global__ __launch_bounds__(256) void kda_seg_scan_kernel(const float *__restri
                 if (dst) dst[(e / 16) * DV + e % 16] = acc[i];
             }
         }
-        __syncthreads();
+        // the next step's M and E reads follow its own barrier
     }
 }
 
@@ -1359,18 +1367,19 @@ static SplitPlan make_plan(const PrefillArgs &a)
     const int slots = cus / 8 > 0 ? cus / 8 : 1;
     const int cx = (int)((chains + 7) / 8);       // chains on the busiest XCD
     const long long L = (a.seqlen + 15) / 16;
-    // cost model, in microseconds: a chunk step of a workgroup (measured on
-    // MI355X at d = 128, about 1.25 us whether 128 or 256 units are busy),
-    // and the correction's HBM traffic at 4 TB/s (o~ and R read, o written;
-    // the plan does not depend on the output type) plus two extra launches
-    const double t_chunk = 1.25;
-    auto cost = [&](long long mk, long long aug_tokens) {
+    // cost model, in microseconds, from MI355X kernel traces at d = 128: a
+    // chunk step of a workgroup (about 1.4 us with every unit busy), the
+    // correction streaming o~ and R in and o out at about 3.5 TB/s (the plan
+    // does not depend on the output type), a scan step, two extra launches
+    const double t_chunk = 1.4;
+    auto cost = [&](long long mk, long long aug_tokens, int ns) {
         double c = (double)mk * t_chunk;
         if (aug_tokens > 0)
-            c += (double)aug_tokens * a.H * (DV * 4 + DK * 4 + DV * 2) / 4.0e6 + 10.0;
+            c += (double)aug_tokens * a.H * (DV * 4 + DK * 4 + DV * 2) / 3.5e6 + 3.0 * ns + 10.0;
         return c;
     };
-    double best = cx * NB <= slots ? cost(L, 0) : cost(sim_makespan(cx, slots, NB, NA, 1, L, L, 0), 0);
+    double best = cx * NB <= slots ? cost(L, 0, 1)
+                                   : cost(sim_makespan(cx, slots, NB, NA, 1, L, L, 0), 0, 1);
     const double base = best;
     if (cx * NB * 2 <= slots) {   // at most half of an XCD busy: a split can pay
         for (int nseg = 2; nseg <= 32; ++nseg) {
@@ -1382,7 +1391,7 @@ static SplitPlan make_plan(const PrefillArgs &a)
                 const int ns = 1 + (int)((L - l0 + ls - 1) / ls);   // no empty segment
                 const long long mk = sim_makespan(cx, slots, NB, NA, ns, L, l0, ls);
                 const long long aug = (long long)a.n_seqs * (a.seqlen - 16 * l0);
-                const double c = cost(mk, aug);
+                const double c = cost(mk, aug, ns);
                 if (c < best) {
                     best = c;
                     pl.nseg = ns;

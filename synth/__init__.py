@@ -30,6 +30,7 @@ from .workloads import (  # noqa: F401
     decode_head_inputs,
     batch_inputs,
     decode_batch_inputs,
+    draft_batch_inputs,
     seq_lengths,
     cu_seqlens,
 )

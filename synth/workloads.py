@@ -260,6 +260,31 @@ def decode_batch_inputs(wl: Workload, threads: Optional[int] = None) -> Dict[str
     return out
 
 
+def draft_batch_inputs(wl: Workload, K: int, stream: int,
+                       threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """K drafted tokens for each of the decode workload's sequences, drawn
+    with the workload's distributions: q, k, g [N, K, H, dk]; v [N, K, H,
+    dv]; beta [N, K, H].  `stream` (>= 1) selects an independent set of
+    streams (sequence index n + stream * N), e.g. one for a step's drafts
+    and another for the previous step's."""
+    N, H, dk, dv = wl.n_seqs, wl.H, wl.dk, wl.dv
+    out = {"q": np.empty((N, K, H, dk), np.float32), "k": np.empty((N, K, H, dk), np.float32),
+           "v": np.empty((N, K, H, dv), np.float32), "g": np.empty((N, K, H, dk), np.float32),
+           "beta": np.empty((N, K, H), np.float32)}
+
+    def work(nh):
+        n, h = nh
+        d = head_inputs(wl, n + stream * N, h, K)
+        for key in ("q", "k", "v", "g"):
+            out[key][n, :, h] = d[key]
+        out["beta"][n, :, h] = d["beta"]
+
+    pairs = [(n, h) for n in range(N) for h in range(H)]
+    with ThreadPoolExecutor(threads or _threads()) as ex:
+        list(ex.map(work, pairs))
+    return out
+
+
 def describe(wl: Workload) -> str:
     L = seq_lengths(wl)
     return (f"{wl.name}: seqs={len(L)} tokens={int(L.sum())} H={wl.H} dk={wl.dk} "
