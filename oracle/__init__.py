@@ -22,8 +22,11 @@ Modules
               used to check the chunk algebra before it is trusted on the GPU
   spec        speculative-decoding verify / replay, as compositions of the
               recurrence
+  prologue    the lower-bounded gate, beta's sigmoid and q/k L2
+              normalisation ahead of the recurrence
 
-Every function is pinned (``tests/test_oracle_pins.py``, ``tests/test_oracle_spec.py``) against facts that
+Every function is pinned (``tests/test_oracle_pins.py``, ``tests/test_oracle_spec.py``,
+``tests/test_oracle_prologue.py``) against facts that
 do not come from the oracle itself (closed forms, a hand-derived example,
 retrieval identities, brute force, invariants); none is "parity unpinned".
 """
@@ -31,3 +34,4 @@ from .recurrence import kda_recurrent, kda_recurrent_varlen, kda_decode_step  # 
 from .transition import kda_transition_bruteforce  # noqa: F401
 from .chunked import kda_chunked  # noqa: F401
 from .spec import kda_spec_verify, kda_spec_commit, kda_spec_step  # noqa: F401
+from .prologue import kda_gate, kda_prologue, kda_gated_recurrent  # noqa: F401
