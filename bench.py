@@ -54,6 +54,12 @@ def prefill_flops(tokens: int, H: int, dk: int, dv: int) -> int:
     return tokens * H * (6 * dk * dv + 16 * (3 * dk + 2 * dv))
 
 
+def gated_prefill_bytes(tokens: int, H: int, dk: int, dv: int, n_seqs: int) -> int:
+    """Algorithmic bytes of the fused-prologue prefill: q, k, z (bf16, d_k),
+    v and o (bf16, d_v), b (bf16) per token-head, A_log, the S_T write."""
+    return tokens * H * (3 * 2 * dk + 2 * 2 * dv + 2) + 4 * H + n_seqs * H * dk * dv * 4
+
+
 def decode_bytes(N: int, H: int, dk: int, dv: int) -> tuple:
     state = N * H * dk * dv * 4 * 2                    # read + write
     other = N * H * (2 * dk * 2 + 2 * dv + 4 * dk + 4 + 2 * dv)
@@ -159,6 +165,8 @@ def main():
     ap.add_argument("--no-split", action="store_true",
                     help="prefill without a workspace: the single-pass kernel only")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the fused-prologue prefill leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -215,6 +223,24 @@ def main():
         kda.kda_fwd_chunked(P["q"], P["k"], P["v"], P["g"], P["beta"], S0=S0, cu_seqlens=cu,
                             o=o, S_T=S_T, workspace=ws)
 
+    # the same prefill with the gate and q/k preprocessing fused in, from
+    # the workload's raw pre-activation draws (A_log = 0); default workload only
+    gated = None
+    if args.workload == "prefill" and not args.no_gated:
+        rb = batch_inputs(wl, raw=True)
+        gated = {key: torch.from_numpy(rb[key]).to(dev).to(dt_in) for key in ("q", "k", "v", "z")}
+        gated["b"] = torch.from_numpy(rb["b"]).to(dev).to(dt_in)
+        shp = (n_seqs, wl.seqlen, wl.H)
+        gated = {key: (t.view(*shp, -1) if t.dim() == 3 else t.view(*shp))
+                 for key, t in gated.items()}
+        gated["A_log"] = torch.zeros(wl.H, device=dev)
+        del rb
+
+    def run_gated():
+        gp = gated
+        kda.kda_fwd_chunked_gated(gp["q"], gp["k"], gp["v"], gp["z"], gp["A_log"], gp["b"],
+                                  o=o, S_T=S_T, workspace=ws)
+
     dec = None
     if not args.no_decode:
         dw = WORKLOADS["decode"]
@@ -263,6 +289,8 @@ def main():
     # ---------------- warmup ----------------
     for _ in range(args.warmup):
         run_prefill()
+        if gated:
+            run_gated()
         if dec:
             run_decode()
             run_spec()
@@ -271,13 +299,17 @@ def main():
 
     # ---------------- timed steps ----------------
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
         run_prefill()
         ev[i][1].record(stream)
+        if gated:
+            ev[i][6].record(stream)
+            run_gated()
+            ev[i][7].record(stream)
         if dec:
             ev[i][2].record(stream)
             run_decode()
@@ -290,6 +322,7 @@ def main():
     pf_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
     dc_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) if dec else None
     sp_ms = np.array([ev[i][4].elapsed_time(ev[i][5]) for i in range(K)]) if dec else None
+    gt_ms = np.array([ev[i][6].elapsed_time(ev[i][7]) for i in range(K)]) if gated else None
     log(f"[bench] prefill ms: mean {pf_ms.mean():.4f} min {pf_ms.min():.4f} "
         f"max {pf_ms.max():.4f}")
 
@@ -327,6 +360,16 @@ def main():
                      "mfma_tflops": alg_f / pf_s / 1e12,
                      "mfma_frac": alg_f / pf_s / 1e12 / BF16_PEAK_TFLOPS},
     }
+    if gated:
+        gt_s = float(gt_ms.mean()) / 1e3
+        gb = gated_prefill_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs)
+        out["gated_prefill"] = {
+            "workload": "the prefill workload from raw q/k, gate pre-activation z and beta "
+                        "pre-activation b (bf16), A_log = 0: gate, beta and L2 norms in-kernel",
+            "launch_ms": gt_s * 1e3, "tokens_per_s": tokens / gt_s,
+            "roofline": {"bound": "hbm", "achieved": gb / gt_s / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gb / gt_s / 1e9 / HBM_PEAK_GBS,
+                         "kernel": "kda_prefill_kernel (gated)", "alg_bytes_per_launch": gb}}
     if dec:
         dw = WORKLOADS["decode"]
         st_b, all_b = decode_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv)

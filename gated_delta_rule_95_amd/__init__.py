@@ -5,6 +5,7 @@ device memory and the current HIP stream; every step of KDA runs in the
 library's hand-written gfx950 kernels.  Names follow the C ABI:
 
     kda_fwd_chunked(q, k, v, g, beta, S0=None, cu_seqlens=None, ...) -> (o, S_T)
+    kda_fwd_chunked_gated(q, k, v, z, A_log, b, ...) -> (o, S_T)   (gate + q/k norm fused)
     kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, dtype) -> int
     kda_decode_step(q, k, v, g, beta, S, ...) -> o        (S updated in place)
     kda_decode_verify(q, k, v, g, beta, S, ...) -> o      (K drafts, S read only)
@@ -20,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
 
-__all__ = ["kda_fwd_chunked", "kda_fwd_workspace_bytes", "kda_decode_step",
+__all__ = ["kda_fwd_chunked", "kda_fwd_chunked_gated", "kda_fwd_workspace_bytes",
+           "kda_decode_step",
            "kda_decode_verify", "kda_decode_commit", "kda_decode_spec", "KDAError",
            "version", "library_path"]
 
@@ -257,3 +259,71 @@ def kda_decode_spec(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                                      N, H, dk, dv, _dt(q.dtype), _dt(od), _ptr(o), _stream(dev))
     _lib.check(st)
     return o
+
+
+def kda_fwd_chunked_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                          A_log: torch.Tensor, b: torch.Tensor,
+                          S0: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None,
+                          out_dtype: Optional[torch.dtype] = None,
+                          output_final_state: bool = True,
+                          o: Optional[torch.Tensor] = None,
+                          S_T: Optional[torch.Tensor] = None,
+                          workspace: Union[None, bool, torch.Tensor] = None,
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill with the gate and q/k preprocessing fused in:
+    q, k unnormalised [..., H, d_k]; z [..., H, d_k] (gate pre-activation,
+    q's dtype); A_log [H] fp32; b [..., H] (beta pre-activation, q's dtype).
+    g = -5 sigmoid(exp(A_log) z), beta = sigmoid(b), q and k L2-normalised
+    in the kernel.  Other arguments as kda_fwd_chunked."""
+    dev = q.device
+    if q.dim() == 4:
+        if cu_seqlens is not None and q.shape[0] != 1:
+            raise ValueError("cu_seqlens needs packed input ([N, H, d] or [1, N, H, d])")
+        lead = tuple(q.shape[:2])
+        n_seqs = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        N, H, dk = q.shape[0] * q.shape[1], q.shape[2], q.shape[3]
+    elif q.dim() == 3:
+        lead = (q.shape[0],)
+        N, H, dk = q.shape
+        n_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    else:
+        raise ValueError("q must be [B, T, H, d_k] or [N, H, d_k]")
+    dv = v.shape[-1]
+    _need(q, "q", device=dev)
+    _need(k, "k", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(v, "v", dtype=q.dtype, shape=lead + (H, dv), device=dev)
+    _need(z, "z", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(b, "b", dtype=q.dtype, shape=lead + (H,), device=dev)
+    _need(A_log, "A_log", dtype=torch.float32, shape=(H,), device=dev)
+    if S0 is not None:
+        _need(S0, "S0", dtype=torch.float32, shape=(n_seqs, H, dk, dv), device=dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+    in_dt = _dt(q.dtype)
+    od = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty(lead + (H, dv), dtype=od, device=dev)
+    else:
+        _need(o, "o", dtype=od, shape=lead + (H, dv), device=dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None:
+        _need(S_T, "S_T", dtype=torch.float32, shape=(n_seqs, H, dk, dv), device=dev)
+    lib = _lib.load()
+    ws, ws_bytes = None, 0
+    if isinstance(workspace, torch.Tensor):
+        _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+        ws, ws_bytes = workspace, workspace.numel()
+    elif workspace is None or workspace is True:
+        need = 0 if (cu_seqlens is not None and n_seqs > 1) else \
+            int(lib.kda_fwd_workspace_bytes(n_seqs, N, H, dk, dv, in_dt))
+        if need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws_bytes = need
+    st = lib.kda_fwd_chunked_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(b),
+                                   _ptr(S0), _ptr(cu_seqlens), n_seqs, N, H, dk, dv, in_dt,
+                                   _dt(od), _ptr(o), _ptr(S_T), _ptr(ws), ws_bytes,
+                                   _stream(dev))
+    _lib.check(st)
+    return o, S_T

@@ -45,6 +45,9 @@ def load() -> ctypes.CDLL:
         lib.kda_fwd_chunked.restype = ctypes.c_int
         lib.kda_fwd_chunked.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                         ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
+        lib.kda_fwd_chunked_gated.restype = ctypes.c_int
+        lib.kda_fwd_chunked_gated.argtypes = [P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                              ctypes.c_int, ctypes.c_int, P, P, P, SZ, P]
         lib.kda_fwd_chunked_noalloc.restype = ctypes.c_int
         lib.kda_fwd_chunked_noalloc.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
                                                 ctypes.c_int, ctypes.c_int, P, P, P]

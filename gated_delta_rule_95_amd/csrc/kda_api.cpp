@@ -143,13 +143,16 @@ namespace {
 const int32_t kPackedMarker = 0;
 }  // namespace
 
-KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
-                                   const float *g, const float *beta, const float *S0,
-                                   const int32_t *cu_seqlens, int32_t n_seqs,
-                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
-                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
-                                   float *S_T, void *workspace, size_t workspace_bytes,
-                                   kda_stream_t stream)
+namespace {
+
+// Shared body of kda_fwd_chunked and kda_fwd_chunked_gated.  Gated: z and b
+// (input type) and A_log replace g and beta, which are then unused.
+kda_status fwd_impl(const char *fn, const void *q, const void *k, const void *v,
+                    const float *g, const float *beta, const void *z, const float *A_log,
+                    const void *b, bool gated, const float *S0, const int32_t *cu_seqlens,
+                    int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                    kda_dtype in_dtype, kda_dtype out_dtype, void *o, float *S_T,
+                    void *workspace, size_t workspace_bytes, kda_stream_t stream)
 {
     kda_status s;
     if ((s = check_dtypes(in_dtype, out_dtype)) != KDA_OK) return s;
@@ -162,6 +165,7 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                     workspace_bytes);
     if (workspace && !aligned(workspace, kWorkspaceAlign))
         return fail(KDA_ERR_INVALID_ARG, "workspace is not %zu-byte aligned", kWorkspaceAlign);
+    if (gated && !A_log) return fail(KDA_ERR_INVALID_ARG, "A_log is NULL");
     if (n_seqs == 0) return ok();
     const int32_t seqlen = cu_seqlens ? 0 : (int32_t)(n_tokens / n_seqs);
     size_t need = 0;
@@ -177,17 +181,20 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     const bool have_tokens = n_tokens > 0;
     const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4, out_b = out_dtype == KDA_BF16 ? 2 : 4;
     const Ptr ps[] = {{q, "q", have_tokens, 2 * in_b}, {k, "k", have_tokens, 2 * in_b},
-                      {v, "v", have_tokens, 4 * in_b}, {g, "g", have_tokens, 8},
-                      {beta, "beta", have_tokens, 4}, {o, "o", have_tokens, 4 * out_b},
-                      {S0, "S0", false, 4}, {S_T, "S_T", false, 4}};
-    if ((s = check_ptrs(ps, 8)) != KDA_OK) return s;
+                      {v, "v", have_tokens, 4 * in_b}, {o, "o", have_tokens, 4 * out_b},
+                      {S0, "S0", false, 4}, {S_T, "S_T", false, 4},
+                      {gated ? z : g, gated ? "z" : "g", have_tokens, gated ? 2 * in_b : 8},
+                      {gated ? b : beta, gated ? "b" : "beta", have_tokens,
+                       gated ? in_b : 4}, {A_log, "A_log", gated, 4}};
+    if ((s = check_ptrs(ps, 9)) != KDA_OK) return s;
     const size_t o_bytes = (size_t)n_tokens * H * d_v * out_b;
     const size_t st_bytes = (size_t)n_seqs * H * d_k * d_v * 4;
-    const void *ins[] = {q, k, v, g, beta, S0};
+    const size_t gb = gated ? in_b : 4;
+    const void *ins[] = {q, k, v, gated ? z : g, gated ? b : beta, S0, gated ? A_log : nullptr};
     const size_t in_sz[] = {(size_t)n_tokens * H * d_k * in_b, (size_t)n_tokens * H * d_k * in_b,
-                            (size_t)n_tokens * H * d_v * in_b, (size_t)n_tokens * H * d_k * 4,
-                            (size_t)n_tokens * H * 4, st_bytes};
-    for (int i = 0; i < 6; ++i) {
+                            (size_t)n_tokens * H * d_v * in_b, (size_t)n_tokens * H * d_k * gb,
+                            (size_t)n_tokens * H * gb, st_bytes, (size_t)H * 4};
+    for (int i = 0; i < 7; ++i) {
         if (overlap(o, o_bytes, ins[i], in_sz[i]) || overlap(S_T, st_bytes, ins[i], in_sz[i]))
             return fail(KDA_ERR_INVALID_ARG, "an output buffer overlaps an input buffer");
         if (overlap(workspace, need, ins[i], in_sz[i]))
@@ -206,7 +213,37 @@ KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
     a.o = o; a.S_T = S_T; a.stream = stream;
     a.workspace = need ? workspace : nullptr;
     a.workspace_bytes = need;
-    return hip_status(kda::launch_prefill(a), "kda_fwd_chunked launch");
+    a.gated = gated; a.z = z; a.b = b; a.A_log = A_log;
+    return hip_status(kda::launch_prefill(a), fn);
+}
+
+}  // namespace
+
+KDA_API kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t n_seqs,
+                                   int64_t n_tokens, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void *o,
+                                   float *S_T, void *workspace, size_t workspace_bytes,
+                                   kda_stream_t stream)
+{
+    return fwd_impl("kda_fwd_chunked launch", q, k, v, g, beta, nullptr, nullptr, nullptr,
+                    false, S0, cu_seqlens, n_seqs, n_tokens, H, d_k, d_v, in_dtype, out_dtype,
+                    o, S_T, workspace, workspace_bytes, stream);
+}
+
+KDA_API kda_status kda_fwd_chunked_gated(const void *q, const void *k, const void *v,
+                                         const void *z, const float *A_log, const void *b,
+                                         const float *S0, const int32_t *cu_seqlens,
+                                         int32_t n_seqs, int64_t n_tokens, int32_t H,
+                                         int32_t d_k, int32_t d_v, kda_dtype in_dtype,
+                                         kda_dtype out_dtype, void *o, float *S_T,
+                                         void *workspace, size_t workspace_bytes,
+                                         kda_stream_t stream)
+{
+    return fwd_impl("kda_fwd_chunked_gated launch", q, k, v, nullptr, nullptr, z, A_log, b,
+                    true, S0, cu_seqlens, n_seqs, n_tokens, H, d_k, d_v, in_dtype, out_dtype,
+                    o, S_T, workspace, workspace_bytes, stream);
 }
 
 KDA_API kda_status kda_decode_step(const void *q, const void *k, const void *v,

@@ -32,6 +32,11 @@ struct PrefillArgs {
     float *S_T;
     void *workspace;             // caller scratch (nullptr: single pass)
     size_t workspace_bytes;
+    // gated prologue (kda_fwd_chunked_gated): z and b in the input type
+    // replace g and beta; A_log [H]; q and k arrive unnormalised
+    bool gated;
+    const void *z, *b;
+    const float *A_log;
     void *stream;
 };
 

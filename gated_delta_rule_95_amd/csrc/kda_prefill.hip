@@ -191,9 +191,13 @@ __device__ __forceinline__ void bstore4(rsrc_t r, int off, f32x4 x, float)
 // ---------------------------------------------------------------------------
 // configuration
 // ---------------------------------------------------------------------------
-template <typename TI, int DK_, int NW_, int NBUF_>
+template <typename TI, int DK_, int NW_, int NBUF_, bool GATED_ = false>
 struct Cfg {
     static constexpr bool BF = std::is_same<TI, bf16>::value;
+    // gated prologue: raw q, k, the gate pre-activation z and beta's
+    // pre-activation b come in (in the input type); the kernel forms
+    // g = -5 sigmoid(e^A z), beta = sigmoid(b) and the L2 scales of q, k
+    static constexpr bool GATED = GATED_;
     using OT = typename std::conditional<BF, bf16, float>::type;   // LDS operand type
     static constexpr int DK = DK_;
     static constexpr int NW = NW_;                 // consumer waves
@@ -259,6 +263,10 @@ struct alignas(16) Buf {
     OT VT[C::BV][C::LVT];                // value block, transposed  [column][token]
     float DEC[C::DK];                    // e^{Gc_16} per channel
     float BETA[16];
+    // gated prologue: per builder wave, the partial sums of q^2 and k^2 of
+    // each token over its channels; then the scales 1 / |q|, 1 / |k|
+    float NRM[C::GATED ? 2 : 1][C::GATED ? C::NBW : 1][16];
+    float SQ[C::GATED ? 16 : 1], SK[C::GATED ? 16 : 1];
 };
 
 // stored position of key channel c in a [16][DK] operand row (see LDK)
@@ -284,10 +292,12 @@ template <class C>
 struct Raw {
     typedef typename std::conditional<C::BF, uint32_t, u32x2>::type P2;   // 2 q/k elements
     P2 q[C::TPG], k[C::TPG];
-    u32x2 g[C::TPG];
+    // log-decay g (fp32 pairs) or, gated, the gate pre-activation z (as q)
+    typename std::conditional<C::GATED, P2, u32x2>::type g[C::TPG];
     // 4 tokens of one v column (bf16: packed pairs, fp32: one per word)
     typename std::conditional<C::BF, u32x2, u32x4>::type v;
     uint32_t beta;
+    int ntok;                             // real tokens of the chunk
 };
 
 template <class C>
@@ -305,20 +315,25 @@ __device__ __forceinline__ float elem(typename Raw<C>::P2 x, int i)
 template <class C, typename TI>
 __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
                                          const TI *__restrict__ k, const TI *__restrict__ v,
-                                         const float *__restrict__ g,
-                                         const float *__restrict__ beta, int64_t tok_base,
+                                         const void *__restrict__ g,
+                                         const void *__restrict__ beta, int64_t tok_base,
                                          int ntok, int ntok_v, int H, int h, int DV,
                                          int col_base, int wave, int lane, int tid)
 {
     constexpr int ES = sizeof(TI);
+    // g and beta: fp32, or (gated) z and b in the input type
+    constexpr int GS = C::GATED ? ES : 4;
     const int rowk = H * C::DK, rowv = H * DV;
     const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * ES);
     const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * ES);
-    const rsrc_t rg = make_rsrc(g + tok_base * rowk, ntok * rowk * 4);
+    const rsrc_t rg = make_rsrc(static_cast<const char *>(g) + tok_base * rowk * GS,
+                                ntok * rowk * GS);
     const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok_v * rowv * ES);
-    const rsrc_t rb = make_rsrc(beta + tok_base * H, ntok * H * 4);
+    const rsrc_t rb = make_rsrc(static_cast<const char *>(beta) + tok_base * H * GS,
+                                ntok * H * GS);
     const int cp = lane % C::CPW, tg = lane / C::CPW;
     const int ch = wave * C::CW + 2 * cp;
+    r.ntok = ntok;
 #pragma unroll
     for (int t = 0; t < C::TPG; ++t) {
         const int e = (tg * C::TPG + t) * rowk + h * C::DK + ch;
@@ -329,9 +344,14 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
             r.q[t] = bload64(rq, e * ES);
             r.k[t] = bload64(rk, e * ES);
         }
-        r.g[t] = bload64(rg, e * 4);
+        if constexpr (!C::GATED) r.g[t] = bload64(rg, e * 4);
+        else if constexpr (C::BF) r.g[t] = bload32(rg, e * ES);
+        else r.g[t] = bload64(rg, e * ES);
     }
-    r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
+    if constexpr (C::GATED && C::BF)
+        r.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, ((tid & 15) * H + h) * ES, 0, 0);
+    else
+        r.beta = bload32(rb, ((tid & 15) * H + h) * 4);
     // v: thread (column c, token quad tq) < NVT loads tokens 4 tq .. 4 tq + 3
     // of column c (a wave's loads of one token are consecutive columns); the
     // condition is uniform over each wave and absent when all builders move v
@@ -386,7 +406,8 @@ __device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &
 // build: raw registers -> end-referenced operands of one chunk in LDS
 // ---------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int lane, int tid)
+__device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int lane, int tid,
+                                      float ea)
 {
     using OT = typename C::OT;
     typedef OT OT2 __attribute__((ext_vector_type(2)));
@@ -402,10 +423,40 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int t = 0; t < TPG; ++t) {
-        s0 = __builtin_fmaf(__uint_as_float(r.g[t][0]), LOG2E, s0);
-        s1 = __builtin_fmaf(__uint_as_float(r.g[t][1]), LOG2E, s1);
+        if constexpr (C::GATED) {
+            // g log2(e) = -5 log2(e) sigmoid(y), y = e^A z: the lower-bounded
+            // gate (K3-on-TPU essay, "KDA + Gated MLA", lower-bounded decay);
+            // y -> -inf gives exp2 = inf, rcp = 0, g = 0, the right limit
+            // a padded token of the ragged tail must stay the identity (g = 0)
+            const float y0 = ea * elem<C>(r.g[t], 0), y1 = ea * elem<C>(r.g[t], 1);
+            const float live = tok0 + t < r.ntok ? -5.f * LOG2E : 0.f;
+            s0 += live * __builtin_amdgcn_rcpf(1.f + fast_exp2(-y0 * LOG2E));
+            s1 += live * __builtin_amdgcn_rcpf(1.f + fast_exp2(-y1 * LOG2E));
+        } else {
+            s0 = __builtin_fmaf(__uint_as_float(r.g[t][0]), LOG2E, s0);
+            s1 = __builtin_fmaf(__uint_as_float(r.g[t][1]), LOG2E, s1);
+        }
         G0[t] = s0;
         G1[t] = s1;
+    }
+    if constexpr (C::GATED) {
+        // partial |q|^2 and |k|^2 of this lane's tokens over the wave's
+        // channels: sum the channel pairs of the CPW lanes of a token group
+#pragma unroll
+        for (int t = 0; t < TPG; ++t) {
+            const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
+            const float ka = elem<C>(r.k[t], 0), kb = elem<C>(r.k[t], 1);
+            float nq = qa * qa + qb * qb, nk = ka * ka + kb * kb;
+#pragma unroll
+            for (int m = 1; m < C::CPW; m <<= 1) {
+                nq += __shfl_xor(nq, m, C::CPW);
+                nk += __shfl_xor(nk, m, C::CPW);
+            }
+            if (cp == 0) {
+                B.NRM[0][wave][tok0 + t] = nq;
+                B.NRM[1][wave][tok0 + t] = nk;
+            }
+        }
     }
     // inclusive scan of the group totals, and the chunk total Gc_16
     float i0, i1, T0, T1;
@@ -503,7 +554,15 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
             else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
         }
     }
-    if (tid < 16) B.BETA[tid] = __uint_as_float(r.beta);
+    if (tid < 16) {
+        if constexpr (C::GATED) {
+            // beta = sigmoid(b)
+            const float b = C::BF ? u16_to_f((uint16_t)r.beta) : __uint_as_float(r.beta);
+            B.BETA[tid] = __builtin_amdgcn_rcpf(1.f + fast_exp2(-b * LOG2E));
+        } else {
+            B.BETA[tid] = __uint_as_float(r.beta);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -641,12 +700,37 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     // A[t][s] = beta_t M[t][s] (s < t), in D layout (a) and transposed (at)
     const float bj = B.BETA[j];
     const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.BETA[4 * g4]);
+    float skj = 1.f;
+    f32x4 sk4 = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (C::GATED) {
+        // L2 scales from the builders' partial sums: k_t = k~_t / |k~_t|
+        // (and q alike) enter A as beta_t s_t s_s M~[t][s], T as
+        // Diag(s_k) T, and the consumer's products as row scales
+        float nq = 0.f, nk = 0.f;
+        f32x4 nk4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < C::NBW; ++w) {
+            nq += B.NRM[0][w][j];
+            nk += B.NRM[1][w][j];
+            nk4 += *reinterpret_cast<const f32x4 *>(&B.NRM[1][w][4 * g4]);
+        }
+        skj = __builtin_amdgcn_rsqf(nk + 1e-6f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sk4[e] = __builtin_amdgcn_rsqf(nk4[e] + 1e-6f);
+        if (g4 == 0) {
+            B.SQ[j] = __builtin_amdgcn_rsqf(nq + 1e-6f);
+            B.SK[j] = skj;
+        }
+    }
+    // beta_t s_t s_s (s = 1 without the gated prologue)
+    const float bsj = bj * skj;
+    const f32x4 bs4 = b4 * sk4;
     f32x4 a, at, id;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = 4 * g4 + e;
-        a[e] = (r > j) ? -b4[e] * mc[e] : 0.f;      // A[r][j]
-        at[e] = (r < j) ? -bj * mt[e] : 0.f;        // A[j][r]
+        a[e] = (r > j) ? -bs4[e] * mc[e] * skj : 0.f;     // A[r][j]
+        at[e] = (r < j) ? -bsj * mt[e] * sk4[e] : 0.f;    // A[j][r]
         id[e] = (r == j) ? 1.f : 0.f;
     }
     const Tile<BF> tA = to_tile<BF>(a), tAT = to_tile<BF>(at);
@@ -667,7 +751,8 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
     const Tile<BF> tA8 = to_tile<BF>(a8), tY2T = to_tile<BF>(y2t);
     const f32x4 tinv = y2t + prod<BF>(tA8, tY2T);
     // T = (I + A)^{-1} Diag(beta): column 4 g4 + e scaled by beta_{4 g4 + e}
-    const f32x4 tv = tinv * b4;
+    f32x4 tv = tinv * b4;
+    if constexpr (C::GATED) tv *= skj;     // Diag(s_k) T
     if constexpr (BF) {
         bf16x4 h, l;
         split4(tv, ne, h, l);
@@ -721,8 +806,9 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const NegEye ne = neg_eye(lane);
     f32x4 x, u, o = zero;
+    // X = V - KE Sd; gated, the product is scaled by s_k per token first
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (float)ah.v[i];
+    for (int i = 0; i < 4; ++i) x[i] = C::GATED ? 0.f : (float)ah.v[i];
     // Sd = Diag(e^{Gc_16}) S
 #pragma unroll
     for (int t = 0; t < C::DK / 16; ++t)
@@ -780,6 +866,11 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             o = mma32(cat(hh, ll), cat(qh, qh), o);          // (Sh + Sl) Qh
             o = mma32(cat(hh, ll), cat(ql, ql), o);          // (Sh + Sl) Ql
         }
+        if constexpr (C::GATED) {
+            const f32x4 sk4 = *reinterpret_cast<const f32x4 *>(&B.SK[4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(sk4[i], x[i], (float)ah.v[i]);
+        }
         // U = T X with both as hi/lo pairs: [Th | Th] and [Tl | Tl] against
         // [Xh; Xl]
         bf16x8 uhh, ull;
@@ -813,6 +904,11 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 o = mma4(S[t][i], B.QH[j][kk], o);           // O^T
             }
         }
+        if constexpr (C::GATED) {
+            const f32x4 sk4 = *reinterpret_cast<const f32x4 *>(&B.SK[4 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = __builtin_fmaf(sk4[i], x[i], (float)ah.v[i]);
+        }
         u = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) u = mma4(B.TH[j][4 * g4 + i], x[i], u);
@@ -824,6 +920,8 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
             for (int i = 0; i < 4; ++i) S[t] = mma4(B.KH[16 * t + j][4 * g4 + i], u[i], S[t]);
         }
     }
+    // gated: O = Diag(s_q) (Q~E Sd + P~ U'), with U' = Diag(s_k) U from T
+    if constexpr (C::GATED) o *= B.SQ[j];
     return o;
 }
 
@@ -896,16 +994,20 @@ struct Params {
     float *entry;   // [chain][nseg-1][d_k][d_v]        entry states of segments 1..
     float *o0;      // [n_seqs][seqlen - len0][H][d_v]  zero-start outputs o~
     float *rq;      // [n_seqs][seqlen - len0][H][d_k]  pulled-back queries R
+    // gated prologue: z [tokens][H][d_k] and b [tokens][H] in the input
+    // type replace g and beta; A_log [H]
+    const TI *z, *braw;
+    const float *A_log;
 };
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
-__global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF>::NT), 1)
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED>
+__global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF, GATED>::NT), 1)
 void kda_prefill_kernel(const Params<TI, TO> p)
 {
-    using C = Cfg<TI, DK, NW, NBUF>;
+    using C = Cfg<TI, DK, NW, NBUF, GATED>;
     constexpr int NB = DV / C::BV;               // value column blocks of a chain
     constexpr int NA = NB + DK / C::BV;          // ... plus transition blocks (split)
     constexpr int LAG = NBUF - 1;            // build runs LAG chunks ahead
@@ -1038,15 +1140,19 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         // NR phases to arrive, and NR sets of raw inputs are in flight.
         constexpr int NR = C::NR;
         Raw<C> r[NR];
+        const void *gsrc = GATED ? static_cast<const void *>(p.z) : p.g;
+        const void *bsrc = GATED ? static_cast<const void *>(p.braw) : p.beta;
+        // e^A of this head (gated prologue)
+        const float ea = GATED ? fast_exp2(p.A_log[h] * LOG2E) : 1.f;
         auto load = [&](Raw<C> &x, int cc) {
-            load_raw<C>(x, p.q, p.k, p.v, p.g, p.beta, bos + 16 * (int64_t)cc, ntok_of(cc),
+            load_raw<C>(x, p.q, p.k, p.v, gsrc, bsrc, bos + 16 * (int64_t)cc, ntok_of(cc),
                         v_on ? ntok_of(cc) : 0, H, h, DV, col_base, bw, lane, btid);
         };
 #pragma unroll
         for (int i = 0; i < NR; ++i) load(r[i], i);
-        if (nch > 0) build<C>(sm.buf[0], r[0], bw, lane, btid);
+        if (nch > 0) build<C>(sm.buf[0], r[0], bw, lane, btid, ea);
         load(r[0], NR);
-        if (nch > 1) build<C>(sm.buf[1], r[1], bw, lane, btid);
+        if (nch > 1) build<C>(sm.buf[1], r[1], bw, lane, btid, ea);
         load(r[1], NR + 1);
         __syncthreads();
         __syncthreads();
@@ -1061,7 +1167,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         for (; c + NR <= nch; c += NR) {
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid);
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, ea);
                 load(r[(i + 2) % NR], c + i + 2 + NR);
                 __syncthreads();
             }
@@ -1069,7 +1175,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
 #pragma unroll
         for (int i = 0; i < NR - 1; ++i) {
             if (c + i < nch) {
-                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid);
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, ea);
                 __syncthreads();
             }
         }
@@ -1417,10 +1523,10 @@ static SplitPlan make_plan(const PrefillArgs &a)
     return pl;
 }
 
-template <typename TI, typename TO, int DK, int DV, int NW, int NBUF>
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED>
 static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan &pl)
 {
-    using C = Cfg<TI, DK, NW, NBUF>;
+    using C = Cfg<TI, DK, NW, NBUF, GATED>;
     static_assert(DV % C::BV == 0, "column blocks");
     constexpr int NB = DV / C::BV, NA = NB + DK / C::BV;
     const int64_t chains8 = ((chains + 7) / 8) * 8;
@@ -1433,6 +1539,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     p.seqlen = a.seqlen; p.n_tokens = (int32_t)a.n_tokens;
     p.n_chains = (int32_t)chains; p.chains8 = (int32_t)chains8; p.H = a.H;
     p.nseg = pl.nseg; p.len0 = pl.len0; p.lenS = pl.lenS;
+    p.z = (const TI *)a.z; p.braw = (const TI *)a.b; p.A_log = a.A_log;
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(a.workspace);
         p.sumst = reinterpret_cast<float *>(ws + pl.off_sumst);
@@ -1441,7 +1548,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
         p.rq = reinterpret_cast<float *>(ws + pl.off_rq);
     }
     hipStream_t st = (hipStream_t)a.stream;
-    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF, GATED>), dim3((unsigned)grid),
                        dim3(C::NT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nseg == 1) return e;
@@ -1461,20 +1568,20 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     return e;
 }
 
-template <typename TI, typename TO, int DK, int DV>
+template <typename TI, typename TO, int DK, int DV, bool GATED>
 static hipError_t launch_dims(const PrefillArgs &a)
 {
     constexpr int NW = PickNW<DK, DV>::value;
     const int64_t chains = (int64_t)a.n_seqs * a.H;
     if (chains == 0) return hipSuccess;
     if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
-    static_assert(sizeof(Smem<Cfg<TI, DK, NW, 3>>) <= 160 * 1024, "LDS");
+    static_assert(sizeof(Smem<Cfg<TI, DK, NW, 3, GATED>>) <= 160 * 1024, "LDS");
     SplitPlan pl;
     if (a.workspace) {
         pl = make_plan<DK, DV>(a);
         if (pl.bytes > a.workspace_bytes) pl = SplitPlan{};   // (checked by the caller)
     }
-    return launch_t<TI, TO, DK, DV, NW, 3>(a, chains, pl);
+    return launch_t<TI, TO, DK, DV, NW, 3, GATED>(a, chains, pl);
 }
 
 template <int DK, int DV>
@@ -1487,11 +1594,11 @@ static size_t plan_bytes(const PrefillArgs &a)
     X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
     X(64, 16) X(64, 32) X(64, 64) X(64, 128) X(128, 16) X(128, 32) X(128, 64) X(128, 128)
 
-template <typename TI, typename TO>
+template <typename TI, typename TO, bool GATED>
 static hipError_t dispatch_dims(const PrefillArgs &a)
 {
 #define KDA_PF_CASE(DK_, DV_) \
-    if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_>(a);
+    if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_, GATED>(a);
     KDA_PF_DIMS(KDA_PF_CASE)
 #undef KDA_PF_CASE
     return hipErrorInvalidValue;
@@ -1506,12 +1613,19 @@ size_t prefill_workspace_bytes(const PrefillArgs &a)
     return 0;
 }
 
-hipError_t launch_prefill(const PrefillArgs &a)
+template <bool GATED>
+static hipError_t dispatch_types(const PrefillArgs &a)
 {
     if (a.in_bf16) {
-        return a.out_bf16 ? dispatch_dims<bf16, bf16>(a) : dispatch_dims<bf16, float>(a);
+        return a.out_bf16 ? dispatch_dims<bf16, bf16, GATED>(a)
+                          : dispatch_dims<bf16, float, GATED>(a);
     }
-    return dispatch_dims<float, float>(a);
+    return dispatch_dims<float, float, GATED>(a);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a)
+{
+    return a.gated ? dispatch_types<true>(a) : dispatch_types<false>(a);
 }
 
 }  // namespace kda

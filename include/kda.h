@@ -154,6 +154,40 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            kda_stream_t stream);
 
 /*
+ * kda_fwd_chunked_gated -- kda_fwd_chunked with the gate and q/k
+ * preprocessing fused into its loads.
+ *
+ * Instead of g, beta and normalised q, k it takes what the model's
+ * projections produce and forms, per token and head:
+ *     q <- q / sqrt(|q|^2 + 1e-6),  k <- k / sqrt(|k|^2 + 1e-6)
+ *     g = -5 sigmoid(exp(A_log[h]) z)   (per key channel)
+ *     beta = sigmoid(b)
+ * The gate is K3's lower-bounded parameterisation (K3-on-TPU essay,
+ * blog.higcp.com, "KDA + Gated MLA", lower-bounded decay: g_min = -5, A a
+ * per-head log-scale); q/k L2 normalisation and the sigmoid branches giving
+ * the per-channel gate and the scalar beta are the Q/K preprocessing the K3
+ * architecture walkthrough describes (mhpq.cn/news/56770, after "KDA 到底在
+ * 算什么").  The epsilon of the normalisation is not given by the pages.
+ * The short causal convolution and Swish that precede the normalisation there
+ * are not included.  Compared with kda_fwd_chunked this reads z in the
+ * input type instead of an fp32 g, and b instead of an fp32 beta.
+ *
+ *   q, k   [n_tokens, H, d_k] in_dtype, unnormalised
+ *   z      [n_tokens, H, d_k] in_dtype, gate pre-activation
+ *   A_log  [H] float32
+ *   b      [n_tokens, H] in_dtype, beta pre-activation
+ * Every other argument, the workspace and the errors are those of
+ * kda_fwd_chunked (kda_fwd_workspace_bytes applies unchanged).  Alignment:
+ * z as q, b one element.
+ */
+kda_status kda_fwd_chunked_gated(const void *q, const void *k, const void *v, const void *z,
+                                 const float *A_log, const void *b, const float *S0,
+                                 const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                                 int32_t H, int32_t d_k, int32_t d_v, kda_dtype in_dtype,
+                                 kda_dtype out_dtype, void *o, float *S_T, void *workspace,
+                                 size_t workspace_bytes, kda_stream_t stream);
+
+/*
  * kda_fwd_workspace_bytes -- scratch size for kda_fwd_chunked.
  *
  * Returns the number of bytes of workspace with which kda_fwd_chunked, called

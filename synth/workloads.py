@@ -145,13 +145,35 @@ def _maybe_bf16(wl: Workload, x: np.ndarray) -> np.ndarray:
     return round_bf16(x) if wl.dtype == "bf16" else x.astype(np.float32)
 
 
-def head_inputs(wl: Workload, n: int, h: int, T: int) -> Dict[str, np.ndarray]:
+def head_inputs(wl: Workload, n: int, h: int, T: int, raw: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of sequence n, head h (T tokens) as fp32 arrays.
 
     q, k : [T, dk]   v : [T, dv]   g : [T, dk]   beta : [T]
     s0   : [dk, dv] or absent.   Values of bf16 workloads are bf16-exact.
+
+    raw=True returns the same streams' draws before the L2 normalisation
+    and the sigmoids: q, k (unnormalised), v, z : [T, dk] (the N(0, g_sigma)
+    draw), b : [T] (the N(0, 1) draw), all in the workload's dtype, for the
+    fused-prologue entry point with A_log = 0 (then g = -5 sigmoid(z) and
+    beta = sigmoid(b) are the workload's distributions).  Not for the
+    stress workloads.
     """
     dk, dv = wl.dk, wl.dv
+    if raw:
+        if wl.stress:
+            raise ValueError("raw inputs are not defined for the stress workloads")
+        q = _rng(wl, n, h, _Q).standard_normal((T, dk), dtype=np.float32)
+        k = _rng(wl, n, h, _K).standard_normal((T, dk), dtype=np.float32)
+        v = _rng(wl, n, h, _V).standard_normal((T, dv), dtype=np.float32)
+        z = _rng(wl, n, h, _G).standard_normal((T, dk), dtype=np.float32) * \
+            np.float32(wl.g_sigma)
+        b = _rng(wl, n, h, _BETA).standard_normal(T, dtype=np.float32)
+        out = {key: _maybe_bf16(wl, x) for key, x in
+               (("q", q), ("k", k), ("v", v), ("z", z), ("b", b))}
+        if wl.s0_sigma is not None:
+            out["s0"] = (_rng(wl, n, h, _S0).standard_normal((dk, dv), dtype=np.float32)
+                         * np.float32(wl.s0_sigma))
+        return out
     q = _unit_rows(_rng(wl, n, h, _Q).standard_normal((T, dk), dtype=np.float32))
     k = _unit_rows(_rng(wl, n, h, _K).standard_normal((T, dk), dtype=np.float32))
     v = _rng(wl, n, h, _V).standard_normal((T, dv), dtype=np.float32)
@@ -192,7 +214,7 @@ def _threads() -> int:
 
 def batch_inputs(wl: Workload, lengths: Optional[np.ndarray] = None,
                  threads: Optional[int] = None,
-                 seqs: Optional[range] = None) -> Dict[str, np.ndarray]:
+                 seqs: Optional[range] = None, raw: bool = False) -> Dict[str, np.ndarray]:
     """Whole packed batch, token-major, fp32 arrays (bf16-exact for bf16).
 
     Returns q, k [N, H, dk]; v [N, H, dv]; g [N, H, dk]; beta [N, H];
@@ -213,10 +235,11 @@ def batch_inputs(wl: Workload, lengths: Optional[np.ndarray] = None,
     cu = cu_seqlens(lengths)
     N, H, dk, dv = int(cu[-1]), wl.H, wl.dk, wl.dv
     ns = len(lengths)
+    gk, bk = ("z", "b") if raw else ("g", "beta")
     out = {
         "q": np.empty((N, H, dk), np.float32), "k": np.empty((N, H, dk), np.float32),
-        "v": np.empty((N, H, dv), np.float32), "g": np.empty((N, H, dk), np.float32),
-        "beta": np.empty((N, H), np.float32),
+        "v": np.empty((N, H, dv), np.float32), gk: np.empty((N, H, dk), np.float32),
+        bk: np.empty((N, H), np.float32),
     }
     if wl.s0_sigma is not None:
         out["s0"] = np.empty((ns, H, dk, dv), np.float32)
@@ -224,10 +247,10 @@ def batch_inputs(wl: Workload, lengths: Optional[np.ndarray] = None,
     def work(nh):
         n, h = nh
         a, b = int(cu[n]), int(cu[n + 1])
-        d = head_inputs(wl, first + n, h, b - a)
-        for key in ("q", "k", "v", "g"):
+        d = head_inputs(wl, first + n, h, b - a, raw=raw)
+        for key in ("q", "k", "v", gk):
             out[key][a:b, h] = d[key]
-        out["beta"][a:b, h] = d["beta"]
+        out[bk][a:b, h] = d[bk]
         if "s0" in d:
             out["s0"][n, h] = d["s0"]
 

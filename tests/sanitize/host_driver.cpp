@@ -108,7 +108,20 @@ int main()
     EXPECT(kda_fwd_chunked(q.data(), k.data(), v.data(), g.data(), beta.data(), nullptr,
                            nullptr, 1, N, H, D, D, (kda_dtype)9, KDA_BF16, o.data(), S.data(),
                            nullptr, 0, nullptr) == KDA_ERR_INVALID_ARG);
-    EXPECT(kda::g_prefill_calls == before);
+    // the gated prologue variant: z as q, b one element per (token, head)
+    std::vector<uint16_t> z(N * H * D), bb(N * H);
+    std::vector<float> A_log(H);
+    EXPECT(kda_fwd_chunked_gated(q.data(), k.data(), v.data(), z.data(), A_log.data(),
+                                 bb.data(), nullptr, nullptr, 1, N, H, D, D, KDA_BF16, KDA_BF16,
+                                 o.data(), S.data(), nullptr, 0, nullptr) == KDA_OK);
+    EXPECT(kda::g_last_prefill.gated && kda::g_last_prefill.z == z.data());
+    EXPECT(kda_fwd_chunked_gated(q.data(), k.data(), v.data(), z.data(), nullptr, bb.data(),
+                                 nullptr, nullptr, 1, N, H, D, D, KDA_BF16, KDA_BF16, o.data(),
+                                 S.data(), nullptr, 0, nullptr) == KDA_ERR_INVALID_ARG);
+    EXPECT(kda_fwd_chunked_gated(q.data(), k.data(), v.data(), z.data(), A_log.data(),
+                                 bb.data(), nullptr, nullptr, 1, N, H, D, D, KDA_BF16, KDA_BF16,
+                                 z.data(), S.data(), nullptr, 0, nullptr) == KDA_ERR_INVALID_ARG);
+    EXPECT(kda::g_prefill_calls == before + 1);
     EXPECT(std::strlen(kda_last_error()) > 0);
     EXPECT(kda_fwd_workspace_bytes(1, N, H, D, D, KDA_BF16) == (size_t)1 << 20);
     EXPECT(kda_fwd_workspace_bytes(-1, N, H, D, D, KDA_BF16) == 0);

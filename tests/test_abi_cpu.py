@@ -17,9 +17,9 @@ def lib():
 def test_exports_match_header(lib):
     declared = _lib.header_functions()
     assert declared == ["kda_decode_commit", "kda_decode_spec", "kda_decode_step",
-                        "kda_decode_verify", "kda_fwd_chunked", "kda_fwd_chunked_noalloc",
-                        "kda_fwd_workspace_bytes", "kda_last_error", "kda_status_string",
-                        "kda_version"]
+                        "kda_decode_verify", "kda_fwd_chunked", "kda_fwd_chunked_gated",
+                        "kda_fwd_chunked_noalloc", "kda_fwd_workspace_bytes", "kda_last_error",
+                        "kda_status_string", "kda_version"]
     for name in declared:
         assert hasattr(lib, name)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -183,3 +183,20 @@ def test_spec_validation(lib):
     assert spec(None, None, None, None, None, 2, P, P * 2, P * 3, P * 4, P * 5, 2, P * 64,
                 1, 1, 16, 16, 1, 1, P * 7, None) == 1
     assert "k_prev is NULL" in _lib.last_error()
+
+
+def test_gated_validation(lib):
+    f = lib.kda_fwd_chunked_gated
+    base = [P, P * 2, P * 3, P * 4, P * 8, P * 5, None, None, 1, 16, 1, 16, 16, 1, 1, P * 6,
+            None, None, 0, None]
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a4=None) == 1 and "A_log is NULL" in _lib.last_error()
+    assert call(a3=None) == 1 and "z is NULL" in _lib.last_error()
+    assert call(a5=None) == 1 and "b is NULL" in _lib.last_error()
+    assert call(a3=P * 4 + 2) == 1 and "aligned" in _lib.last_error()
+    assert call(a15=P * 4) == 1 and "overlaps" in _lib.last_error()
+    assert call(a8=0, a9=0) == 0

@@ -67,3 +67,20 @@ def test_decode_inputs():
     d = decode_head_inputs(wl, 3, 7)
     assert d["S"].shape == (128, 128) and d["q"].shape == (128,)
     assert 0.04 < d["S"].std() < 0.06
+
+
+def test_raw_draws_are_the_prologue_inputs():
+    """raw=True gives the draws behind the regular inputs: normalising q, k
+    and mapping z, b through the gate and sigmoid (on the host, here) gives
+    back the regular fp32 workload inputs before bf16 rounding."""
+    wl = WORKLOADS["long_prefill"]
+    r = head_inputs(wl, 0, 3, 50, raw=True)
+    d = head_inputs(wl, 0, 3, 50)
+    assert set(r) == {"q", "k", "v", "z", "b", "s0"}
+    assert np.array_equal(r["v"], d["v"]) and np.array_equal(r["s0"], d["s0"])
+    g = -5.0 / (1.0 + np.exp(-r["z"].astype(np.float64)))
+    assert np.max(np.abs(g - d["g"])) < 0.05          # z is bf16-rounded in raw mode
+    qn = r["q"] / np.linalg.norm(r["q"], axis=1, keepdims=True)
+    assert np.max(np.abs(qn - d["q"])) < 2e-2
+    b = batch_inputs(WORKLOADS["prefill"], raw=True, seqs=range(1, 2))
+    assert set(b) >= {"q", "k", "v", "z", "b", "cu_seqlens"}
