@@ -403,6 +403,29 @@ __device__ __forceinline__ void group_scan(float x, int tg, float &incl, float &
 }
 
 // ---------------------------------------------------------------------------
+// Sum over each aligned group of N = 8 or 16 lanes, left in every lane of the
+// group: a butterfly of data-parallel-primitive lane moves inside a 16-lane
+// row (swap neighbours, swap pairs, mirror the half row, mirror the row),
+// each folded into a vector add; no LDS round trip.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x)
+{
+    static_assert(N == 8 || N == 16, "lane groups of 8 or 16");
+    x += dpp_mov<0xB1>(x);                        // quad_perm [1,0,3,2]
+    x += dpp_mov<0x4E>(x);                        // quad_perm [2,3,0,1]
+    x += dpp_mov<0x141>(x);                       // row_half_mirror
+    if constexpr (N == 16) x += dpp_mov<0x140>(x); // row_mirror
+    return x;
+}
+
+// ---------------------------------------------------------------------------
 // build: raw registers -> end-referenced operands of one chunk in LDS
 // ---------------------------------------------------------------------------
 template <class C>
@@ -447,11 +470,8 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
             const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
             const float ka = elem<C>(r.k[t], 0), kb = elem<C>(r.k[t], 1);
             float nq = qa * qa + qb * qb, nk = ka * ka + kb * kb;
-#pragma unroll
-            for (int m = 1; m < C::CPW; m <<= 1) {
-                nq += __shfl_xor(nq, m, C::CPW);
-                nk += __shfl_xor(nk, m, C::CPW);
-            }
+            nq = group_sum<C::CPW>(nq);
+            nk = group_sum<C::CPW>(nk);
             if (cp == 0) {
                 B.NRM[0][wave][tok0 + t] = nq;
                 B.NRM[1][wave][tok0 + t] = nk;
