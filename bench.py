@@ -30,9 +30,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 SPEC_K = 4                       # drafts per speculative step (previous and new)
 SEED_ACCEPT = 0x4B4441 + 17      # seeded acceptance counts of the speculative leg
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix, published
-PROFILE_PMC = os.path.join(ROOT, "profiles", "kda_prefill_pmc.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_95_amd", "csrc", f)
-                  for f in ("kda_prefill.hip", "kda_device.h")]
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -76,28 +74,31 @@ def spec_bytes(N: int, H: int, dk: int, dv: int, K: int, K_prev: int) -> tuple:
     return state, state + prev + new + 4 * N
 
 
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(workload: str):
-    """HBM bytes per prefill launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and on this
-    workload (None otherwise)."""
+def counter_record(workload: str, kernel: str):
+    """The committed rocprofv3 counter summary of `kernel` (a class name of
+    profile_summary.kernel_class) on `workload`, or None: only a record
+    taken on the current kernel sources and on this very workload counts."""
+    from profile_summary import source_hash
     try:
-        with open(PROFILE_PMC) as f:
+        with open(os.path.join(PROFILE_DIR, f"pmc_{workload}.json")) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != source_hash():
+    if rec.get("kernel_source_sha256_16") != source_hash() or rec.get("workload") != workload:
         return None
-    if rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("kernels", {}).get(kernel)
+
+
+def attach_counters(roofline: dict, workload: str, kernel: str) -> dict:
+    """traffic = HBM bytes per dispatch from the counter record (null without
+    one); the matrix-core and vector-ALU busy fractions ride along."""
+    k = counter_record(workload, kernel)
+    roofline["traffic"] = None if k is None else k.get("hbm_bytes_per_dispatch")
+    if k is not None and "mfma_busy_pct" in k:
+        roofline["counters"] = {key: k[key] for key in
+                                ("mfma_busy_pct", "valu_busy_pct", "lds_bank_conflict_pct",
+                                 "mfma_bf16_flops") if key in k}
+    return roofline
 
 
 def host_cpu() -> dict:
@@ -330,7 +331,6 @@ def main():
     alg_b = prefill_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs, S0 is not None)
     alg_f = prefill_flops(tokens, wl.H, wl.dk, wl.dv)
     achieved = alg_b / pf_s / 1e9
-    traffic = measured_traffic(args.workload)
     out = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, 1xMI355X, % roofline",
         "value": tokens / pf_s,
@@ -354,12 +354,13 @@ def main():
                    if dec else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic,
+                     "traffic": None,
                      "kernel": "kda_prefill_kernel", "alg_bytes_per_launch": alg_b,
                      "launch_ms": pf_s * 1e3,
                      "mfma_tflops": alg_f / pf_s / 1e12,
                      "mfma_frac": alg_f / pf_s / 1e12 / BF16_PEAK_TFLOPS},
     }
+    attach_counters(out["roofline"], args.workload, "prefill")
     if gated:
         gt_s = float(gt_ms.mean()) / 1e3
         gb = gated_prefill_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs)
@@ -370,6 +371,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": gb / gt_s / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gb / gt_s / 1e9 / HBM_PEAK_GBS,
                          "kernel": "kda_prefill_kernel (gated)", "alg_bytes_per_launch": gb}}
+        attach_counters(out["gated_prefill"]["roofline"], args.workload, "prefill_gated")
     if dec:
         dw = WORKLOADS["decode"]
         st_b, all_b = decode_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv)
@@ -381,6 +383,7 @@ def main():
                                       "frac": all_b / dc_s / 1e9 / HBM_PEAK_GBS,
                                       "kernel": "kda_decode_kernel",
                                       "alg_bytes_per_launch": all_b}}
+        attach_counters(out["decode"]["roofline"], args.workload, "decode")
         sst_b, sall_b = spec_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv, SPEC_K, SPEC_K)
         sp_s = float(sp_ms.mean()) / 1e3
         out["spec_decode"] = {
@@ -391,6 +394,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": sall_b / sp_s / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": sall_b / sp_s / 1e9 / HBM_PEAK_GBS,
                          "kernel": "kda_spec_kernel", "alg_bytes_per_launch": sall_b}}
+        attach_counters(out["spec_decode"]["roofline"], args.workload, "spec")
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(threads)

@@ -2,24 +2,59 @@
 under profiles/.
 
   python profile_summary.py stats <trace_dir> <out.md> "<command>"
-      kernel-trace statistics (rocprofv3 --kernel-trace --stats) as a table
-  python profile_summary.py pmc <fetch_dir> <write_dir> <copy_mib> <out.json> "<commands>"
-      HBM bytes per prefill launch from one FETCH_SIZE and one WRITE_SIZE
-      pass over the default bench workload (prefill), each scaled by what the
-      same counter reads for the plain device copy of <copy_mib> MiB that
-      `bench.py --calib-copy-mib` runs
+      kernel-trace statistics (rocprofv3 --kernel-trace --stats
+      --output-format csv) as a table
+  python profile_summary.py pmc <out.json> <workload> <copy_mib> "<commands>" \\
+                                <fetch_dir> <write_dir> [<sq_dir>]
+      per kernel of the run: HBM bytes per dispatch from one FETCH_SIZE and
+      one WRITE_SIZE pass, each scaled by what the same counter reads for the
+      plain device copy of <copy_mib> MiB that `bench.py --calib-copy-mib`
+      runs; with <sq_dir>, the SQ pass of SQ_COUNTERS below turned into
+      matrix-core busy, vector-ALU busy and LDS bank-conflict fractions
 
 The JSON records the hash of the kernel sources it was taken on; bench.py
-reports the traffic only while that hash matches.
+uses a record only while that hash matches and only for its own workload.
 """
 import csv
 import glob
+import hashlib
 import json
 import os
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PREFILL = "kda_prefill_kernel"
+CSRC = os.path.join(ROOT, "gated_delta_rule_95_amd", "csrc")
+
+# MI355X: 256 compute units, 4 SIMDs each
+CU_NUM, SIMD_NUM = 256, 1024
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
+               "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+               "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+
+
+def kernel_class(name: str):
+    """Which of the library's kernels (or the calibration copy) a dispatch is."""
+    if "copyBuffer" in name:
+        return "copy"
+    if "kda_prefill_kernel" in name:
+        # the last template argument is the gated-prologue flag
+        return "prefill_gated" if "Lb1E" in name else "prefill"
+    for key in ("kda_decode_kernel", "kda_spec_kernel", "kda_seg_scan_kernel",
+                "kda_seg_correct_kernel"):
+        if key in name:
+            return key.replace("kda_", "").replace("_kernel", "")
+    return None
+
+
+def source_hash() -> str:
+    """sha256 (16 hex digits) over every kernel source of the library."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if p.endswith((".hip", ".h", ".cpp")):
+            with open(p, "rb") as f:
+                h.update(os.path.basename(p).encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _rows(d, pattern):
@@ -41,7 +76,8 @@ def stats(trace_dir, out_md, command):
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     for r in rows:
         name = r["Name"]
-        short = name.split("(")[0][:90]
+        cls = kernel_class(name)
+        short = (cls + ": " if cls else "") + name.split("(")[0][:80]
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
@@ -50,45 +86,75 @@ def stats(trace_dir, out_md, command):
     print("\n".join(lines))
 
 
-def _counter(d, counter):
-    """{kernel name: [value per dispatch]} for one counter (KiB per dispatch)."""
-    per = {}
+def _counters(d):
+    """{(kernel class, dispatch id): {counter: value summed over instances}}."""
     acc = {}
     for r in _rows(d, "*counter_collection.csv"):
-        if r["Counter_Name"] != counter:
+        cls = kernel_class(r["Kernel_Name"])
+        if cls is None:
             continue
-        key = (r["Kernel_Name"], r["Dispatch_Id"])
-        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
-    for (name, _), v in acc.items():
-        per.setdefault(name, []).append(v)
-    return per
+        key = (cls, r["Dispatch_Id"])
+        c = acc.setdefault(key, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return acc
 
 
-def _pick(per, pred):
-    vals = [v for name, vs in per.items() if pred(name) for v in vs]
-    if not vals:
-        raise SystemExit("kernel not found in counter output")
-    vals.sort()
-    return vals[len(vals) // 2]
+def _median(vals):
+    vals = sorted(vals)
+    return vals[len(vals) // 2] if vals else None
 
 
-def pmc(fetch_dir, write_dir, copy_mib, out_json, commands):
-    sys.path.insert(0, ROOT)
-    from bench import source_hash
+def _per_class(acc, counter):
+    per = {}
+    for (cls, _), c in acc.items():
+        if counter in c:
+            per.setdefault(cls, []).append(c[counter])
+    return {cls: _median(v) for cls, v in per.items()}
+
+
+def pmc(out_json, workload, copy_mib, commands, fetch_dir, write_dir, sq_dir=None):
     copy_bytes = int(copy_mib) * (1 << 20)
-    is_copy = lambda n: "copyBuffer" in n                             # noqa: E731
-    is_pf = lambda n: PREFILL in n                                   # noqa: E731
-    fe, wr = _counter(fetch_dir, "FETCH_SIZE"), _counter(write_dir, "WRITE_SIZE")
-    cf, cw = _pick(fe, is_copy) * 1024, _pick(wr, is_copy) * 1024
-    pf, pw = _pick(fe, is_pf) * 1024, _pick(wr, is_pf) * 1024
-    rf, rw = copy_bytes / cf, copy_bytes / cw
-    rec = {"kernel": PREFILL, "workload": "prefill",
-           "fetch_bytes_raw": pf, "write_bytes_raw": pw,
-           "copy_bytes": copy_bytes, "copy_fetch_raw": cf, "copy_write_raw": cw,
-           "fetch_scale": rf, "write_scale": rw,
-           "hbm_bytes_per_launch": pf * rf + pw * rw,
-           "kernel_source_sha256_16": source_hash(),
-           "commands": commands}
+    fe = _per_class(_counters(fetch_dir), "FETCH_SIZE")
+    wr = _per_class(_counters(write_dir), "WRITE_SIZE")
+    if "copy" not in fe or "copy" not in wr:
+        raise SystemExit("the calibration copy is missing from the counter output")
+    rf, rw = copy_bytes / (fe["copy"] * 1024), copy_bytes / (wr["copy"] * 1024)
+    rec = {"workload": workload, "kernel_source_sha256_16": source_hash(),
+           "copy_bytes": copy_bytes, "copy_fetch_raw": fe["copy"] * 1024,
+           "copy_write_raw": wr["copy"] * 1024, "fetch_scale": rf, "write_scale": rw,
+           "commands": commands, "kernels": {}}
+    for cls in sorted(set(fe) | set(wr)):
+        if cls == "copy":
+            continue
+        k = rec["kernels"].setdefault(cls, {})
+        if cls in fe:
+            k["fetch_bytes"] = fe[cls] * 1024 * rf
+        if cls in wr:
+            k["write_bytes"] = wr[cls] * 1024 * rw
+        if cls in fe and cls in wr:
+            k["hbm_bytes_per_dispatch"] = k["fetch_bytes"] + k["write_bytes"]
+    if sq_dir:
+        acc = _counters(sq_dir)
+        per = {name: _per_class(acc, name) for name in SQ_COUNTERS}
+        for cls in per["GRBM_GUI_ACTIVE"]:
+            if cls == "copy":
+                continue
+            gui = per["GRBM_GUI_ACTIVE"][cls]
+            k = rec["kernels"].setdefault(cls, {})
+            raw = {name: per[name].get(cls) for name in SQ_COUNTERS}
+            k["sq_raw"] = raw
+            # rocprofv3's derived metrics: MfmaUtil, VALUBusy, LDSBankConflict
+            if gui:
+                k["mfma_busy_pct"] = 100.0 * (raw["SQ_VALU_MFMA_BUSY_CYCLES"] or 0) / (gui * SIMD_NUM)
+                k["valu_busy_pct"] = 100.0 * (raw["SQ_ACTIVE_INST_VALU"] or 0) / CU_NUM / gui
+                k["lds_bank_conflict_pct"] = 100.0 * (raw["SQ_LDS_BANK_CONFLICT"] or 0) / gui / CU_NUM
+            if raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] is not None:
+                k["mfma_bf16_flops"] = raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        rec["sq_counters"] = SQ_COUNTERS
+        rec["sq_note"] = ("GRBM_GUI_ACTIVE and the SQ counters are summed over the "
+                          "instances rocprofv3 reports; the percentages use rocprofv3's "
+                          "MfmaUtil, VALUBusy and LDSBankConflict expressions with "
+                          f"CU_NUM = {CU_NUM}, SIMD_NUM = {SIMD_NUM}")
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -98,7 +164,7 @@ def pmc(fetch_dir, write_dir, copy_mib, out_json, commands):
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "stats" and len(sys.argv) == 5:
         stats(*sys.argv[2:])
-    elif len(sys.argv) >= 2 and sys.argv[1] == "pmc" and len(sys.argv) == 7:
+    elif len(sys.argv) >= 2 and sys.argv[1] == "pmc" and len(sys.argv) in (8, 9):
         pmc(*sys.argv[2:])
     else:
         raise SystemExit(__doc__)

@@ -30,35 +30,57 @@ def test_decode_bytes():
     assert total - state == 256 * 64 * 1540
 
 
+def test_gated_and_spec_bytes():
+    # q, k, z (bf16, d_k), v, o (bf16, d_v), b (bf16): 1282 B per token-head
+    assert bench.gated_prefill_bytes(1, 1, 128, 128, 0) == 1282 + 4
+    state, total = bench.spec_bytes(2, 3, 128, 128, 4, 4)
+    assert state == 2 * 3 * 128 * 128 * 8
+    assert total - state == 2 * 4 * 3 * (2 * 128 + 2 * 128 + 4 * 128 + 4) + \
+        2 * 4 * 3 * 1540 + 4 * 2
+
+
 @pytest.fixture
 def record(tmp_path, monkeypatch):
-    path = tmp_path / "pmc.json"
-    monkeypatch.setattr(bench, "PROFILE_PMC", str(path))
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    import profile_summary
 
-    def write(**kw):
-        rec = {"kernel": "kda_prefill_kernel", "workload": "prefill",
-               "hbm_bytes_per_launch": 123.0,
-               "kernel_source_sha256_16": bench.source_hash()}
+    def write(file_workload="prefill", **kw):
+        rec = {"workload": file_workload,
+               "kernel_source_sha256_16": profile_summary.source_hash(),
+               "kernels": {"prefill": {"hbm_bytes_per_dispatch": 123.0, "mfma_busy_pct": 30.0,
+                                       "valu_busy_pct": 40.0},
+                           "decode": {"hbm_bytes_per_dispatch": 7.0}}}
         rec.update(kw)
-        path.write_text(json.dumps(rec))
+        (tmp_path / f"pmc_{file_workload}.json").write_text(json.dumps(rec))
     return write
 
 
-def test_traffic_only_for_matching_source_and_workload(record):
+def test_counters_only_for_matching_source_workload_and_kernel(record):
     record()
-    assert bench.measured_traffic("prefill") == 123.0
+    r = bench.attach_counters({}, "prefill", "prefill")
+    assert r["traffic"] == 123.0 and r["counters"]["mfma_busy_pct"] == 30.0
+    assert bench.attach_counters({}, "prefill", "decode") == {"traffic": 7.0}
+    assert bench.attach_counters({}, "prefill", "spec") == {"traffic": None}
     # counters taken on the prefill workload say nothing about other workloads
-    assert bench.measured_traffic("long_prefill") is None
-    assert bench.measured_traffic("varlen") is None
+    assert bench.attach_counters({}, "long_prefill", "prefill") == {"traffic": None}
     # a record taken on other kernel sources is stale
     record(kernel_source_sha256_16="0" * 16)
-    assert bench.measured_traffic("prefill") is None
-    # a record that does not name its workload is not trusted
-    record(workload=None)
-    assert bench.measured_traffic("prefill") is None
+    assert bench.attach_counters({}, "prefill", "prefill") == {"traffic": None}
+    # a record filed under another workload's name is not trusted
+    record(workload="varlen")
+    assert bench.counter_record("prefill", "prefill") is None
 
 
-def test_traffic_missing_record(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "PROFILE_PMC", str(tmp_path / "absent.json"))
-    assert bench.measured_traffic("prefill") is None
+def test_counters_missing_record(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.counter_record("prefill", "prefill") is None
 
+
+def test_kernel_classes():
+    import profile_summary as ps
+    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb0EEEvNS_6"
+                           "ParamsIT_T0_EE") == "prefill"
+    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb1EEEvNS_6"
+                           "ParamsIT_T0_EE") == "prefill_gated"
+    assert ps.kernel_class("void kda::kda_seg_scan_kernel<128, 128>(float const*)") == "seg_scan"
+    assert ps.kernel_class("__amd_rocclr_copyBuffer") == "copy"
