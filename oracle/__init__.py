@@ -24,9 +24,11 @@ Modules
               recurrence
   prologue    the lower-bounded gate, beta's sigmoid and q/k L2
               normalisation ahead of the recurrence
+  backward    reverse-mode gradients of the recurrence (dq, dk, dv, dg,
+              dbeta, dS0)
 
 Every function is pinned (``tests/test_oracle_pins.py``, ``tests/test_oracle_spec.py``,
-``tests/test_oracle_prologue.py``) against facts that
+``tests/test_oracle_prologue.py``, ``tests/test_oracle_backward.py``) against facts that
 do not come from the oracle itself (closed forms, a hand-derived example,
 retrieval identities, brute force, invariants); none is "parity unpinned".
 """
@@ -35,3 +37,4 @@ from .transition import kda_transition_bruteforce  # noqa: F401
 from .chunked import kda_chunked  # noqa: F401
 from .spec import kda_spec_verify, kda_spec_commit, kda_spec_step  # noqa: F401
 from .prologue import kda_gate, kda_prologue, kda_gated_recurrent  # noqa: F401
+from .backward import kda_recurrent_vjp, kda_recurrent_vjp_varlen  # noqa: F401
