@@ -7,6 +7,7 @@ library's hand-written gfx950 kernels.  Names follow the C ABI:
     kda_fwd_chunked(q, k, v, g, beta, S0=None, cu_seqlens=None, ...) -> (o, S_T)
     kda_fwd_chunked_gated(q, k, v, z, A_log, b, ...) -> (o, S_T)   (gate + q/k norm fused)
     kda_fwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v, dtype) -> int
+    kda_bwd_chunked(q, k, v, g, beta, dO, S0=None, dS_T=None, ...) -> (dq, dk, dv, dg, dbeta, dS0)
     kda_decode_step(q, k, v, g, beta, S, ...) -> o        (S updated in place)
     kda_decode_verify(q, k, v, g, beta, S, ...) -> o      (K drafts, S read only)
     kda_decode_commit(k, v, g, beta, n_accept, S)         (replay accepted, S in place)
@@ -22,6 +23,7 @@ from . import _lib
 from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
 
 __all__ = ["kda_fwd_chunked", "kda_fwd_chunked_gated", "kda_fwd_workspace_bytes",
+           "kda_bwd_chunked",
            "kda_decode_step",
            "kda_decode_verify", "kda_decode_commit", "kda_decode_spec", "KDAError",
            "version", "library_path"]
@@ -327,3 +329,56 @@ def kda_fwd_chunked_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: 
                                    _stream(dev))
     _lib.check(st)
     return o, S_T
+
+
+def kda_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, dO: torch.Tensor, S0: Optional[torch.Tensor] = None,
+                    dS_T: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, ...]:
+    """Gradients of kda_fwd_chunked: (dq, dk, dv, dg, dbeta, dS0), fp32, the
+    inputs' shapes; dO has o's shape and q's dtype, dS_T the final state's
+    (or None).  The workspace (uint8) is allocated through torch unless
+    given."""
+    dev = q.device
+    if q.dim() == 4:
+        if cu_seqlens is not None and q.shape[0] != 1:
+            raise ValueError("cu_seqlens needs packed input ([N, H, d] or [1, N, H, d])")
+        lead = tuple(q.shape[:2])
+        n_seqs = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        N, H, dk = q.shape[0] * q.shape[1], q.shape[2], q.shape[3]
+    elif q.dim() == 3:
+        lead = (q.shape[0],)
+        N, H, dk = q.shape
+        n_seqs = 1 if cu_seqlens is None else cu_seqlens.numel() - 1
+    else:
+        raise ValueError("q must be [B, T, H, d_k] or [N, H, d_k]")
+    dv = v.shape[-1]
+    _need(q, "q", device=dev)
+    _need(k, "k", dtype=q.dtype, shape=q.shape, device=dev)
+    _need(v, "v", dtype=q.dtype, shape=lead + (H, dv), device=dev)
+    _need(g, "g", dtype=torch.float32, shape=lead + (H, dk), device=dev)
+    _need(beta, "beta", dtype=torch.float32, shape=lead + (H,), device=dev)
+    _need(dO, "dO", dtype=q.dtype, shape=lead + (H, dv), device=dev)
+    st_shape = (n_seqs, H, dk, dv)
+    if S0 is not None:
+        _need(S0, "S0", dtype=torch.float32, shape=st_shape, device=dev)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", dtype=torch.float32, shape=st_shape, device=dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
+    lib = _lib.load()
+    need = int(lib.kda_bwd_workspace_bytes(n_seqs, N, H, dk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+    f32 = lambda shape: torch.empty(shape, dtype=torch.float32, device=dev)   # noqa: E731
+    dq, dkk, dg = f32(lead + (H, dk)), f32(lead + (H, dk)), f32(lead + (H, dk))
+    dvv, db, dS0 = f32(lead + (H, dv)), f32(lead + (H,)), f32(st_shape)
+    st = lib.kda_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+                             _ptr(cu_seqlens), n_seqs, N, H, dk, dv, _dt(q.dtype), _ptr(dO),
+                             _ptr(dS_T), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db),
+                             _ptr(dS0), _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check(st)
+    return dq, dkk, dvv, dg, db, dS0

@@ -65,6 +65,11 @@ def load() -> ctypes.CDLL:
         lib.kda_decode_spec.restype = ctypes.c_int
         lib.kda_decode_spec.argtypes = [P, P, P, P, P, I32, P, P, P, P, P, I32, P, I32, I32,
                                         I32, I32, ctypes.c_int, ctypes.c_int, P, P]
+        lib.kda_bwd_workspace_bytes.restype = SZ
+        lib.kda_bwd_workspace_bytes.argtypes = [I32, I64, I32, I32, I32]
+        lib.kda_bwd_chunked.restype = ctypes.c_int
+        lib.kda_bwd_chunked.argtypes = [P, P, P, P, P, P, P, I32, I64, I32, I32, I32,
+                                        ctypes.c_int, P, P, P, P, P, P, P, P, P, SZ, P]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_status_string.argtypes = [ctypes.c_int]
         lib.kda_last_error.restype = ctypes.c_char_p

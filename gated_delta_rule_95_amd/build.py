@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 ARCH = "gfx950"
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_noalloc.hip",
-           "kda_spec.hip"]
+           "kda_spec.hip", "kda_backward.hip"]
 
 
 def hipcc() -> str:

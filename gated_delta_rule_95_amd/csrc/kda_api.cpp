@@ -422,6 +422,92 @@ KDA_API kda_status kda_decode_spec(const void *k_prev, const void *v_prev, const
     return run_spec(a, "kda_decode_spec launch");
 }
 
+namespace {
+
+// chunk slots (bos / 16 + n + c) of a batch: an upper bound on every slot + 1
+int64_t bwd_slots(int32_t n_seqs, int64_t n_tokens) { return n_tokens / 16 + n_seqs + 1; }
+
+}  // namespace
+
+KDA_API size_t kda_bwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                                       int32_t d_v)
+{
+    if (check_fwd_sizes(n_seqs, n_tokens, H, d_k, d_v, true) != KDA_OK) return 0;
+    if (n_seqs == 0) return 0;
+    const size_t slots = (size_t)bwd_slots(n_seqs, n_tokens);
+    const size_t ck = slots * H * d_k * d_v * 4;
+    const size_t part = slots * H * kda::bwd_part_floats(d_k, d_v) * 4;
+    return ((ck + 255) & ~(size_t)255) + ((part + 255) & ~(size_t)255);
+}
+
+KDA_API kda_status kda_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *S0,
+                                   const int32_t *cu_seqlens, int32_t n_seqs, int64_t n_tokens,
+                                   int32_t H, int32_t d_k, int32_t d_v, kda_dtype in_dtype,
+                                   const void *dO, const float *dS_T, float *dq, float *dk,
+                                   float *dv, float *dg, float *dbeta, float *dS0,
+                                   void *workspace, size_t workspace_bytes, kda_stream_t stream)
+{
+    kda_status s;
+    if ((s = check_dtypes(in_dtype, in_dtype)) != KDA_OK) return s;
+    if ((s = check_fwd_sizes(n_seqs, n_tokens, H, d_k, d_v, cu_seqlens != nullptr)) != KDA_OK)
+        return s;
+    if (cu_seqlens && !aligned(cu_seqlens, 4))
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens is not 4-byte aligned");
+    if (n_seqs == 0) return ok();
+    const size_t need = kda_bwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v);
+    if (!workspace) return fail(KDA_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned(workspace, kWorkspaceAlign))
+        return fail(KDA_ERR_INVALID_ARG, "workspace is not %zu-byte aligned", kWorkspaceAlign);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_INVALID_ARG,
+                    "workspace_bytes %zu is below the %zu bytes kda_bwd_workspace_bytes gives",
+                    workspace_bytes, need);
+    const bool tok = n_tokens > 0;
+    const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4;
+    const Ptr ps[] = {{q, "q", tok, in_b}, {k, "k", tok, in_b}, {v, "v", tok, in_b},
+                      {g, "g", tok, 4}, {beta, "beta", tok, 4}, {dO, "dO", tok, in_b},
+                      {S0, "S0", false, 4}, {dS_T, "dS_T", false, 4}, {dq, "dq", tok, 4},
+                      {dk, "dk", tok, 4}, {dv, "dv", tok, 4}, {dg, "dg", tok, 4},
+                      {dbeta, "dbeta", tok, 4}, {dS0, "dS0", false, 4}};
+    if ((s = check_ptrs(ps, 14)) != KDA_OK) return s;
+    const size_t nk = (size_t)n_tokens * H * d_k, nv = (size_t)n_tokens * H * d_v;
+    const size_t st = (size_t)n_seqs * H * d_k * d_v * 4;
+    // written spans first: the gradients and the workspace
+    const Span all[] = {{dq, nk * 4}, {dk, nk * 4}, {dv, nv * 4}, {dg, nk * 4},
+                        {dbeta, (size_t)n_tokens * H * 4}, {dS0, st}, {workspace, need},
+                        {q, nk * in_b}, {k, nk * in_b}, {v, nv * in_b}, {g, nk * 4},
+                        {beta, (size_t)n_tokens * H * 4}, {dO, nv * in_b}, {S0, st},
+                        {dS_T, st}};
+    if (spans_overlap(all, 7, 15))
+        return fail(KDA_ERR_INVALID_ARG, "kda_bwd_chunked: an output or the workspace overlaps "
+                                         "another argument");
+    char *ws = static_cast<char *>(workspace);
+    const size_t slots = (size_t)bwd_slots(n_seqs, n_tokens);
+    float *ckpt = reinterpret_cast<float *>(ws);
+    float *part = reinterpret_cast<float *>(
+        ws + ((slots * H * d_k * d_v * 4 + 255) & ~(size_t)255));
+    const int32_t seqlen = cu_seqlens ? 0 : (int32_t)(n_tokens / n_seqs);
+    // 1. the forward, keeping the state at every chunk start
+    kda::PrefillArgs f{};
+    f.q = q; f.k = k; f.v = v; f.g = g; f.beta = beta; f.S0 = S0;
+    f.cu_seqlens = cu_seqlens; f.n_seqs = n_seqs; f.n_tokens = n_tokens; f.seqlen = seqlen;
+    f.H = H; f.d_k = d_k; f.d_v = d_v;
+    f.in_bf16 = in_dtype == KDA_BF16; f.out_bf16 = f.in_bf16;
+    f.o = nullptr; f.S_T = nullptr; f.ckpt = ckpt; f.skip_o = true; f.stream = stream;
+    if ((s = hip_status(kda::launch_prefill(f), "kda_bwd_chunked forward launch")) != KDA_OK)
+        return s;
+    // 2. the reverse sweep and the per-chunk finish
+    kda::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.dO = dO; a.g = g; a.beta = beta; a.dST = dS_T;
+    a.cu_seqlens = cu_seqlens; a.n_seqs = n_seqs; a.n_tokens = n_tokens; a.seqlen = seqlen;
+    a.H = H; a.d_k = d_k; a.d_v = d_v; a.in_bf16 = in_dtype == KDA_BF16;
+    a.ckpt = ckpt; a.part = part; a.n_slots = (int64_t)slots;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    a.stream = stream;
+    return hip_status(kda::launch_bwd(a), "kda_bwd_chunked launch");
+}
+
 KDA_API const char *kda_status_string(kda_status s)
 {
     switch (s) {

@@ -37,6 +37,10 @@ struct PrefillArgs {
     bool gated;
     const void *z, *b;
     const float *A_log;
+    // backward support (single pass only): state checkpoints at every chunk
+    // start, slot bos / 16 + n + c; o not written when skip_o
+    float *ckpt;
+    bool skip_o;
     void *stream;
 };
 
@@ -59,8 +63,28 @@ struct SpecArgs {
     void *stream;
 };
 
+// Chunked backward (kda_bwd_chunked): the sweep over column blocks and the
+// per-chunk finisher; ckpt holds the forward's chunk-start states, part the
+// blocks' partial sums, both indexed by chunk slot bos / 16 + n + c.
+struct BwdArgs {
+    const void *q, *k, *v, *dO;
+    const float *g, *beta, *dST;
+    const int32_t *cu_seqlens;
+    int32_t n_seqs;
+    int64_t n_tokens;
+    int32_t seqlen, H, d_k, d_v;
+    bool in_bf16;
+    float *ckpt, *part;
+    int64_t n_slots;
+    float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+    void *stream;
+};
+// floats of partial sums per (chunk slot, head)
+size_t bwd_part_floats(int32_t d_k, int32_t d_v);
+
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_spec(const SpecArgs &a);
+hipError_t launch_bwd(const BwdArgs &a);
 // Bytes of workspace the sequence-split path needs for these sizes on the
 // current device (0: the single-pass kernel is used).  Reads only the size
 // fields of `a` (and whether cu_seqlens is set).

@@ -1018,6 +1018,11 @@ struct Params {
     // type replace g and beta; A_log [H]
     const TI *z, *braw;
     const float *A_log;
+    // backward support: the state at the start of every chunk, to
+    // ckpt[bos / 16 + n + c][H][d_k][d_v] (c the chunk of sequence n); o
+    // stores skipped when skip_o
+    float *ckpt;
+    bool skip_o;
 };
 
 // ---------------------------------------------------------------------------
@@ -1233,7 +1238,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         f32x4 ov = {0.f, 0.f, 0.f, 0.f};
         auto store_o = [&](int cc) {
             const rsrc_t ro = make_rsrc(obase + 16 * (int64_t)cc * orow,
-                                        (cc >= 0 ? ntok_of(cc) : 0) * ow);
+                                        (cc >= 0 && !p.skip_o ? ntok_of(cc) : 0) * ow);
             if (out_f32) bstore4(ro, ooff, ov, float{});
             else bstore4(ro, ooff, ov, TO{});
         };
@@ -1241,9 +1246,20 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         __syncthreads();
         Ahead<C> ah;
         read_ahead<C>(sm.buf[0], ah, wave, lane);
+        // checkpoint slots of this sequence (backward support)
+        float *ck = p.ckpt ? p.ckpt + ((bos / 16 + n) * H + h) * (int64_t)(DK * DV) + col_base +
+                                 col
+                           : nullptr;
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             store_o(c - 1);
+            if (ck) {
+#pragma unroll
+                for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ck[(int64_t)c * H * DK * DV + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
+            }
             ov = consume<C>(slot(c % 3), S, ah, wave, lane);
             read_ahead<C>(slot((c + 1) % 3), ah, wave, lane);
             __syncthreads();
@@ -1560,6 +1576,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     p.n_chains = (int32_t)chains; p.chains8 = (int32_t)chains8; p.H = a.H;
     p.nseg = pl.nseg; p.len0 = pl.len0; p.lenS = pl.lenS;
     p.z = (const TI *)a.z; p.braw = (const TI *)a.b; p.A_log = a.A_log;
+    p.ckpt = a.ckpt; p.skip_o = a.skip_o;
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(a.workspace);
         p.sumst = reinterpret_cast<float *>(ws + pl.off_sumst);

@@ -300,6 +300,35 @@ kda_status kda_decode_spec(const void *k_prev, const void *v_prev, const float *
                            int32_t d_k, int32_t d_v, kda_dtype in_dtype, kda_dtype out_dtype,
                            void *o, kda_stream_t stream);
 
+/*
+ * kda_bwd_chunked -- gradients of kda_fwd_chunked.
+ *
+ * Given the forward's inputs and the cotangents dO of o ([n_tokens, H, d_v],
+ * in_dtype) and dS_T of the final states (float32 [n_seqs, H, d_k, d_v], or
+ * NULL for zero), writes float32 gradients with the inputs' layouts:
+ * dq, dk, dg [n_tokens, H, d_k]; dv [n_tokens, H, d_v]; dbeta [n_tokens, H];
+ * dS0 [n_seqs, H, d_k, d_v] (skipped when NULL).  A backward pass (custom
+ * VJP) is one of the parts of the KDA kernel suite the K3-on-TPU essay
+ * describes (blog.higcp.com, the section on the existing TPU kernel).
+ *
+ * It reruns the forward keeping the state at every 16-token chunk start,
+ * then walks the chunks backwards carrying the cotangent of the state, by
+ * blocks of state columns, and finishes each chunk's dq, dk, dg and dbeta in
+ * a second, chunk-parallel pass.  Arithmetic is fp32 throughout.  The
+ * workspace (required) must hold kda_bwd_workspace_bytes(...) bytes, 256-byte
+ * aligned: the checkpoints (64 KiB per chunk and head at d = 128) and the
+ * blocks' partial sums.  Other arguments, layouts and errors as for
+ * kda_fwd_chunked.
+ */
+size_t kda_bwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                               int32_t d_v);
+kda_status kda_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *S0, const int32_t *cu_seqlens,
+                           int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
+                           int32_t d_v, kda_dtype in_dtype, const void *dO, const float *dS_T,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                           void *workspace, size_t workspace_bytes, kda_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *kda_status_string(kda_status s);
 

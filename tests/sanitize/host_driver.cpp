@@ -23,7 +23,7 @@ void kda_oracle_head(int64_t T, int dk, int dv, const float *q, const float *k,
 }
 
 namespace kda {
-static int g_prefill_calls = 0, g_decode_calls = 0, g_spec_calls = 0;
+static int g_prefill_calls = 0, g_decode_calls = 0, g_spec_calls = 0, g_bwd_calls = 0;
 static SpecArgs g_last_spec;
 static PrefillArgs g_last_prefill;
 size_t prefill_workspace_bytes(const PrefillArgs &a)
@@ -40,6 +40,12 @@ hipError_t launch_prefill(const PrefillArgs &a)
 hipError_t launch_decode(const DecodeArgs &)
 {
     ++g_decode_calls;
+    return hipSuccess;
+}
+size_t bwd_part_floats(int32_t d_k, int32_t d_v) { return (size_t)d_k * d_v; }
+hipError_t launch_bwd(const BwdArgs &)
+{
+    ++g_bwd_calls;
     return hipSuccess;
 }
 hipError_t launch_spec(const SpecArgs &a)
@@ -156,6 +162,27 @@ int main()
     EXPECT(kda_decode_commit(k.data(), v.data(), g.data(), beta.data(), nullptr, S.data(), 2, 4,
                              H, D, D, KDA_BF16, nullptr) == KDA_ERR_INVALID_ARG);
     EXPECT(kda::g_spec_calls == 3);
+    // backward: the forward with checkpoints, then the sweep and finish
+    {
+        std::vector<float> gq(N * H * D), gk(N * H * D), gv(N * H * D), gg(N * H * D),
+            gb(N * H);
+        const size_t need = kda_bwd_workspace_bytes(1, N, H, D, D);
+        std::vector<unsigned char> wsb(need + 256);
+        void *wsp = reinterpret_cast<void *>(
+            (reinterpret_cast<uintptr_t>(wsb.data()) + 255) & ~(uintptr_t)255);
+        const int pf = kda::g_prefill_calls;
+        EXPECT(kda_bwd_chunked(q.data(), k.data(), v.data(), g.data(), beta.data(), nullptr,
+                               nullptr, 1, N, H, D, D, KDA_BF16, o.data(), nullptr, gq.data(),
+                               gk.data(), gv.data(), gg.data(), gb.data(), nullptr, wsp, need,
+                               nullptr) == KDA_OK);
+        EXPECT(kda::g_prefill_calls == pf + 1 && kda::g_last_prefill.ckpt != nullptr &&
+               kda::g_last_prefill.skip_o && kda::g_bwd_calls == 1);
+        EXPECT(kda_bwd_chunked(q.data(), k.data(), v.data(), g.data(), beta.data(), nullptr,
+                               nullptr, 1, N, H, D, D, KDA_BF16, o.data(), nullptr, gq.data(),
+                               gq.data(), gv.data(), gg.data(), gb.data(), nullptr, wsp, need,
+                               nullptr) == KDA_ERR_INVALID_ARG);          // dk overlaps dq
+        EXPECT(kda::g_bwd_calls == 1);
+    }
     EXPECT(std::strcmp(kda_status_string(KDA_ERR_HIP), "KDA_ERR_HIP") == 0);
     EXPECT(std::strcmp(kda_status_string((kda_status)42), "KDA_ERR_UNKNOWN") == 0);
     EXPECT(std::strstr(kda_version(), "gfx950") != nullptr);

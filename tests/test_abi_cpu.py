@@ -16,10 +16,11 @@ def lib():
 
 def test_exports_match_header(lib):
     declared = _lib.header_functions()
-    assert declared == ["kda_decode_commit", "kda_decode_spec", "kda_decode_step",
-                        "kda_decode_verify", "kda_fwd_chunked", "kda_fwd_chunked_gated",
-                        "kda_fwd_chunked_noalloc", "kda_fwd_workspace_bytes", "kda_last_error",
-                        "kda_status_string", "kda_version"]
+    assert declared == ["kda_bwd_chunked", "kda_bwd_workspace_bytes", "kda_decode_commit",
+                        "kda_decode_spec", "kda_decode_step", "kda_decode_verify",
+                        "kda_fwd_chunked", "kda_fwd_chunked_gated", "kda_fwd_chunked_noalloc",
+                        "kda_fwd_workspace_bytes", "kda_last_error", "kda_status_string",
+                        "kda_version"]
     for name in declared:
         assert hasattr(lib, name)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
@@ -200,3 +201,24 @@ def test_gated_validation(lib):
     assert call(a3=P * 4 + 2) == 1 and "aligned" in _lib.last_error()
     assert call(a15=P * 4) == 1 and "overlaps" in _lib.last_error()
     assert call(a8=0, a9=0) == 0
+
+
+def test_bwd_validation(lib):
+    f = lib.kda_bwd_chunked
+    need = lib.kda_bwd_workspace_bytes(1, 32, 1, 16, 16)
+    assert need > 0 and need % 256 == 0
+    # every slot (32 / 16 + 1 + 1 = 4) holds a 16 x 16 checkpoint
+    assert need >= 4 * 16 * 16 * 4
+    base = [P, P * 2, P * 3, P * 4, P * 5, None, None, 1, 32, 1, 16, 16, 1, P * 6, None,
+            P * 7, P * 8, P * 9, P * 10, P * 11, None, P * 16, need, None]
+    def call(**kw):
+        a = list(base)
+        for i, val in kw.items():
+            a[int(i[1:])] = val
+        return f(*a)
+    assert call(a21=None) == 1 and "workspace is NULL" in _lib.last_error()
+    assert call(a22=need - 256) == 1 and "below" in _lib.last_error()
+    assert call(a21=P * 16 + 64) == 1 and "aligned" in _lib.last_error()
+    assert call(a13=None) == 1 and "dO is NULL" in _lib.last_error()
+    assert call(a15=P) == 1 and "overlaps" in _lib.last_error()
+    assert call(a7=0, a8=0) == 0
