@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 SPEC_K = 4                       # drafts per speculative step (previous and new)
 SEED_ACCEPT = 0x4B4441 + 17      # seeded acceptance counts of the speculative leg
+SEED_COTANGENT = 0x4B4441 + 23   # seeded cotangents of the backward leg
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 matrix, published
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -74,19 +75,31 @@ def spec_bytes(N: int, H: int, dk: int, dv: int, K: int, K_prev: int) -> tuple:
     return state, state + prev + new + 4 * N
 
 
+def backward_bytes(tokens: int, H: int, dk: int, dv: int, n_seqs: int, s0: bool) -> int:
+    """Algorithmic HBM bytes of one kda_bwd_chunked call: read q, k, v, dO
+    (bf16), g (fp32 [N,H,dk]), beta, S0 and dS_T once; write dq, dk, dg (fp32
+    [N,H,dk]), dv (fp32 [N,H,dv]), dbeta and dS0 once.  Checkpointed chunk
+    states and per-chunk partials are the implementation's own traffic."""
+    per_tok = H * ((2 * dk + 2 * dv) * 2 + dk * 4 + 4 + 3 * dk * 4 + dv * 4 + 4)
+    st = n_seqs * H * dk * dv * 4
+    return tokens * per_tok + st * (3 if s0 else 2)
+
+
 def counter_record(workload: str, kernel: str):
     """The committed rocprofv3 counter summary of `kernel` (a class name of
     profile_summary.kernel_class) on `workload`, or None: only a record
-    taken on the current kernel sources and on this very workload counts."""
+    taken on this kernel's current sources and on this very workload counts."""
     from profile_summary import source_hash
     try:
         with open(os.path.join(PROFILE_DIR, f"pmc_{workload}.json")) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != source_hash() or rec.get("workload") != workload:
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("workload") != workload or not k or \
+            k.get("source_sha256_16") != source_hash(kernel):
         return None
-    return rec.get("kernels", {}).get(kernel)
+    return k
 
 
 def attach_counters(roofline: dict, workload: str, kernel: str) -> dict:
@@ -168,6 +181,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the fused-prologue prefill leg")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the chunked-backward leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -242,6 +257,21 @@ def main():
         kda.kda_fwd_chunked_gated(gp["q"], gp["k"], gp["v"], gp["z"], gp["A_log"], gp["b"],
                                   o=o, S_T=S_T, workspace=ws)
 
+    # the chunked backward of the same prefill, with seeded random cotangents
+    # dO (o's shape and dtype) and dS_T; its workspace allocated once here
+    bwd = None
+    if args.workload == "prefill" and not args.no_backward:
+        r = np.random.default_rng(SEED_COTANGENT)
+        bwd = {"dO": torch.from_numpy(r.standard_normal(tuple(o.shape), np.float32)).to(dev)
+               .to(dt_in),
+               "dS_T": torch.from_numpy(r.standard_normal(tuple(S_T.shape), np.float32)).to(dev)}
+        bwd["ws"] = torch.empty(kda.kda_bwd_workspace_bytes(n_seqs, tokens, wl.H, wl.dk,
+                                                            wl.dv), dtype=torch.uint8, device=dev)
+
+    def run_backward():
+        kda.kda_bwd_chunked(P["q"], P["k"], P["v"], P["g"], P["beta"], bwd["dO"], S0=S0,
+                            dS_T=bwd["dS_T"], cu_seqlens=cu, workspace=bwd["ws"])
+
     dec = None
     if not args.no_decode:
         dw = WORKLOADS["decode"]
@@ -292,6 +322,8 @@ def main():
         run_prefill()
         if gated:
             run_gated()
+        if bwd:
+            run_backward()
         if dec:
             run_decode()
             run_spec()
@@ -300,7 +332,7 @@ def main():
 
     # ---------------- timed steps ----------------
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(K)]
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     for i in range(K):
@@ -311,6 +343,10 @@ def main():
             ev[i][6].record(stream)
             run_gated()
             ev[i][7].record(stream)
+        if bwd:
+            ev[i][8].record(stream)
+            run_backward()
+            ev[i][9].record(stream)
         if dec:
             ev[i][2].record(stream)
             run_decode()
@@ -324,6 +360,7 @@ def main():
     dc_ms = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) if dec else None
     sp_ms = np.array([ev[i][4].elapsed_time(ev[i][5]) for i in range(K)]) if dec else None
     gt_ms = np.array([ev[i][6].elapsed_time(ev[i][7]) for i in range(K)]) if gated else None
+    bw_ms = np.array([ev[i][8].elapsed_time(ev[i][9]) for i in range(K)]) if bwd else None
     log(f"[bench] prefill ms: mean {pf_ms.mean():.4f} min {pf_ms.min():.4f} "
         f"max {pf_ms.max():.4f}")
 
@@ -372,6 +409,17 @@ def main():
                          "unit": "GB/s", "frac": gb / gt_s / 1e9 / HBM_PEAK_GBS,
                          "kernel": "kda_prefill_kernel (gated)", "alg_bytes_per_launch": gb}}
         attach_counters(out["gated_prefill"]["roofline"], args.workload, "prefill_gated")
+    if bwd:
+        bw_s = float(bw_ms.mean()) / 1e3
+        bb = backward_bytes(tokens, wl.H, wl.dk, wl.dv, n_seqs, S0 is not None)
+        out["backward"] = {
+            "workload": "gradients of the prefill workload (dq, dk, dv, dg, dbeta, dS0, fp32) "
+                        "from seeded bf16 dO and fp32 dS_T: checkpointing forward, reverse "
+                        "sweep and per-chunk finisher, timed as one call",
+            "launch_ms": bw_s * 1e3, "tokens_per_s": tokens / bw_s,
+            "roofline": {"bound": "hbm", "achieved": bb / bw_s / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": bb / bw_s / 1e9 / HBM_PEAK_GBS,
+                         "kernel": "kda_bwd_chunked (3 kernels)", "alg_bytes_per_launch": bb}}
     if dec:
         dw = WORKLOADS["decode"]
         st_b, all_b = decode_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv)

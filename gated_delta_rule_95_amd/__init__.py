@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import KDAError, KDA_BF16, KDA_F32, KDA_OK  # noqa: F401
 
 __all__ = ["kda_fwd_chunked", "kda_fwd_chunked_gated", "kda_fwd_workspace_bytes",
-           "kda_bwd_chunked",
+           "kda_bwd_chunked", "kda_bwd_workspace_bytes",
            "kda_decode_step",
            "kda_decode_verify", "kda_decode_commit", "kda_decode_spec", "KDAError",
            "version", "library_path"]
@@ -331,6 +331,11 @@ def kda_fwd_chunked_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: 
     return o, S_T
 
 
+def kda_bwd_workspace_bytes(n_seqs: int, n_tokens: int, H: int, d_k: int, d_v: int) -> int:
+    """Bytes of workspace kda_bwd_chunked needs for these sizes."""
+    return int(_lib.load().kda_bwd_workspace_bytes(n_seqs, n_tokens, H, d_k, d_v))
+
+
 def kda_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                     beta: torch.Tensor, dO: torch.Tensor, S0: Optional[torch.Tensor] = None,
                     dS_T: Optional[torch.Tensor] = None,
@@ -368,7 +373,7 @@ def kda_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", dtype=torch.int32, device=dev)
     lib = _lib.load()
-    need = int(lib.kda_bwd_workspace_bytes(n_seqs, N, H, dk, dv))
+    need = kda_bwd_workspace_bytes(n_seqs, N, H, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     else:

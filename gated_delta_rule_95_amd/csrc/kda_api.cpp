@@ -494,7 +494,7 @@ KDA_API kda_status kda_bwd_chunked(const void *q, const void *k, const void *v, 
     f.cu_seqlens = cu_seqlens; f.n_seqs = n_seqs; f.n_tokens = n_tokens; f.seqlen = seqlen;
     f.H = H; f.d_k = d_k; f.d_v = d_v;
     f.in_bf16 = in_dtype == KDA_BF16; f.out_bf16 = f.in_bf16;
-    f.o = nullptr; f.S_T = nullptr; f.ckpt = ckpt; f.skip_o = true; f.stream = stream;
+    f.o = nullptr; f.S_T = nullptr; f.ckpt = ckpt; f.stream = stream;
     if ((s = hip_status(kda::launch_prefill(f), "kda_bwd_chunked forward launch")) != KDA_OK)
         return s;
     // 2. the reverse sweep and the per-chunk finish

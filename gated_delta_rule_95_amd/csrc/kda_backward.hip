@@ -214,10 +214,13 @@ void kda_bwd_sweep(const TI *__restrict__ q, const TI *__restrict__ k,
         const int nt = (int)(T - (int64_t)c * C < C ? T - (int64_t)c * C : C);
         __syncthreads();
         chunk_ops<TI, DK>(sm.o, q, k, g, beta, tok0, nt, H, h);
-        const float *ck = ckpt + ((slot0 + c) * H + h) * (int64_t)(DK * DV) + col0;
+        // the checkpoint's 16 x 16 tiles: element (row i, column c) of tile
+        // (c / 16, i / 16) sits at lane (c % 16) + 16 ((i % 16) / 4), word i % 4
+        const float *ck = ckpt + ((slot0 + c) * H + h) * (int64_t)(DK * DV);
         for (int e = tid; e < DK * BV; e += NT) {
-            const int i = e / BV, j = e % BV;
-            sm.S[i][j] = ck[(int64_t)i * DV + j];
+            const int i = e / BV, j = e % BV, cc = col0 + j;
+            sm.S[i][j] = ck[(((cc / 16) * (DK / 16) + i / 16) * WAVE + (cc % 16) +
+                            16 * ((i % 16) / 4)) * 4 + i % 4];
         }
         for (int e = tid; e < C * BV; e += NT) {
             const int r = e / BV, j = e % BV;

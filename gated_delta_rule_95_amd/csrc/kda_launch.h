@@ -37,10 +37,10 @@ struct PrefillArgs {
     bool gated;
     const void *z, *b;
     const float *A_log;
-    // backward support (single pass only): state checkpoints at every chunk
-    // start, slot bos / 16 + n + c; o not written when skip_o
+    // non-null: the checkpointing forward of the backward pass (single pass,
+    // not gated, o not written): the state at every chunk start goes to
+    // slot bos / 16 + n + c, in 16 x 16 tiles (layout at the prefill kernel)
     float *ckpt;
-    bool skip_o;
     void *stream;
 };
 

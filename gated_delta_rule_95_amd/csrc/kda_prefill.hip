@@ -1018,20 +1018,22 @@ struct Params {
     // type replace g and beta; A_log [H]
     const TI *z, *braw;
     const float *A_log;
-    // backward support: the state at the start of every chunk, to
-    // ckpt[bos / 16 + n + c][H][d_k][d_v] (c the chunk of sequence n); o
-    // stores skipped when skip_o
+    // checkpointing variant (backward support): the state at the start of
+    // every chunk c of sequence n goes to slot bos / 16 + n + c of ckpt, as
+    // [slot][H][d_v / 16][d_k / 16][64][4] floats: per 16 x 16 tile (key rows
+    // 16 t .., value columns 16 cb ..), lane j + 16 g of the tile holds rows
+    // 16 t + 4 g .. + 3 of column 16 cb + j; o is not written
     float *ckpt;
-    bool skip_o;
 };
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED>
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED, bool CKPT>
 __global__ __launch_bounds__((Cfg<TI, DK, NW, NBUF, GATED>::NT), 1)
 void kda_prefill_kernel(const Params<TI, TO> p)
 {
+    static_assert(!(CKPT && GATED), "the checkpointing variant takes g and beta");
     using C = Cfg<TI, DK, NW, NBUF, GATED>;
     constexpr int NB = DV / C::BV;               // value column blocks of a chain
     constexpr int NA = NB + DK / C::BV;          // ... plus transition blocks (split)
@@ -1238,7 +1240,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         f32x4 ov = {0.f, 0.f, 0.f, 0.f};
         auto store_o = [&](int cc) {
             const rsrc_t ro = make_rsrc(obase + 16 * (int64_t)cc * orow,
-                                        (cc >= 0 && !p.skip_o ? ntok_of(cc) : 0) * ow);
+                                        (cc >= 0 && !CKPT ? ntok_of(cc) : 0) * ow);
             if (out_f32) bstore4(ro, ooff, ov, float{});
             else bstore4(ro, ooff, ov, TO{});
         };
@@ -1246,19 +1248,18 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         __syncthreads();
         Ahead<C> ah;
         read_ahead<C>(sm.buf[0], ah, wave, lane);
-        // checkpoint slots of this sequence (backward support)
-        float *ck = p.ckpt ? p.ckpt + ((bos / 16 + n) * H + h) * (int64_t)(DK * DV) + col_base +
-                                 col
-                           : nullptr;
+        // checkpoint tiles of this wave's 16 columns, chunk 0 of the sequence
+        f32x4 *ck = nullptr;
+        if constexpr (CKPT)
+            ck = reinterpret_cast<f32x4 *>(p.ckpt + ((bos / 16 + n) * H + h) * (int64_t)(DK * DV)) +
+                 ((col_base / 16 + wave) * (DK / 16)) * WAVE + lane;
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             store_o(c - 1);
-            if (ck) {
+            if constexpr (CKPT) {
 #pragma unroll
                 for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        ck[(int64_t)c * H * DK * DV + (int64_t)(16 * t + 4 * g4 + i) * DV] = S[t][i];
+                    ck[(int64_t)c * H * (DK * DV / 4) + t * WAVE] = S[t];
             }
             ov = consume<C>(slot(c % 3), S, ah, wave, lane);
             read_ahead<C>(slot((c + 1) % 3), ah, wave, lane);
@@ -1559,7 +1560,7 @@ static SplitPlan make_plan(const PrefillArgs &a)
     return pl;
 }
 
-template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED>
+template <typename TI, typename TO, int DK, int DV, int NW, int NBUF, bool GATED, bool CKPT>
 static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan &pl)
 {
     using C = Cfg<TI, DK, NW, NBUF, GATED>;
@@ -1576,7 +1577,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     p.n_chains = (int32_t)chains; p.chains8 = (int32_t)chains8; p.H = a.H;
     p.nseg = pl.nseg; p.len0 = pl.len0; p.lenS = pl.lenS;
     p.z = (const TI *)a.z; p.braw = (const TI *)a.b; p.A_log = a.A_log;
-    p.ckpt = a.ckpt; p.skip_o = a.skip_o;
+    p.ckpt = a.ckpt;
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(a.workspace);
         p.sumst = reinterpret_cast<float *>(ws + pl.off_sumst);
@@ -1585,7 +1586,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
         p.rq = reinterpret_cast<float *>(ws + pl.off_rq);
     }
     hipStream_t st = (hipStream_t)a.stream;
-    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF, GATED>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((kda_prefill_kernel<TI, TO, DK, DV, NW, NBUF, GATED, CKPT>), dim3((unsigned)grid),
                        dim3(C::NT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || pl.nseg == 1) return e;
@@ -1605,7 +1606,7 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     return e;
 }
 
-template <typename TI, typename TO, int DK, int DV, bool GATED>
+template <typename TI, typename TO, int DK, int DV, bool GATED, bool CKPT>
 static hipError_t launch_dims(const PrefillArgs &a)
 {
     constexpr int NW = PickNW<DK, DV>::value;
@@ -1614,11 +1615,11 @@ static hipError_t launch_dims(const PrefillArgs &a)
     if (chains > INT32_MAX - 8) return hipErrorInvalidValue;
     static_assert(sizeof(Smem<Cfg<TI, DK, NW, 3, GATED>>) <= 160 * 1024, "LDS");
     SplitPlan pl;
-    if (a.workspace) {
+    if (!CKPT && a.workspace) {
         pl = make_plan<DK, DV>(a);
         if (pl.bytes > a.workspace_bytes) pl = SplitPlan{};   // (checked by the caller)
     }
-    return launch_t<TI, TO, DK, DV, NW, 3, GATED>(a, chains, pl);
+    return launch_t<TI, TO, DK, DV, NW, 3, GATED, CKPT>(a, chains, pl);
 }
 
 template <int DK, int DV>
@@ -1631,11 +1632,11 @@ static size_t plan_bytes(const PrefillArgs &a)
     X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(32, 16) X(32, 32) X(32, 64) X(32, 128) \
     X(64, 16) X(64, 32) X(64, 64) X(64, 128) X(128, 16) X(128, 32) X(128, 64) X(128, 128)
 
-template <typename TI, typename TO, bool GATED>
+template <typename TI, typename TO, bool GATED, bool CKPT = false>
 static hipError_t dispatch_dims(const PrefillArgs &a)
 {
 #define KDA_PF_CASE(DK_, DV_) \
-    if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_, GATED>(a);
+    if (a.d_k == DK_ && a.d_v == DV_) return launch_dims<TI, TO, DK_, DV_, GATED, CKPT>(a);
     KDA_PF_DIMS(KDA_PF_CASE)
 #undef KDA_PF_CASE
     return hipErrorInvalidValue;
@@ -1662,6 +1663,13 @@ static hipError_t dispatch_types(const PrefillArgs &a)
 
 hipError_t launch_prefill(const PrefillArgs &a)
 {
+    if (a.ckpt) {
+        // checkpointing forward of the backward pass: g and beta given, no
+        // output, no split
+        if (a.gated) return hipErrorInvalidValue;
+        return a.in_bf16 ? dispatch_dims<bf16, bf16, false, true>(a)
+                         : dispatch_dims<float, float, false, true>(a);
+    }
     return a.gated ? dispatch_types<true>(a) : dispatch_types<false>(a);
 }
 

@@ -12,14 +12,16 @@ under profiles/.
       runs; with <sq_dir>, the SQ pass of SQ_COUNTERS below turned into
       matrix-core busy, vector-ALU busy and LDS bank-conflict fractions
 
-The JSON records the hash of the kernel sources it was taken on; bench.py
-uses a record only while that hash matches and only for its own workload.
+The JSON records, per kernel, the hash of the sources that kernel is built
+from; bench.py uses a kernel's figures only while that hash matches and
+only for the record's own workload.
 """
 import csv
 import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -37,23 +39,36 @@ def kernel_class(name: str):
     if "copyBuffer" in name:
         return "copy"
     if "kda_prefill_kernel" in name:
-        # the last template argument is the gated-prologue flag
-        return "prefill_gated" if "Lb1E" in name else "prefill"
+        # the last two template arguments: gated prologue, checkpointing
+        m = re.search(r"Lb([01])ELb([01])E", name)
+        if m and m.group(2) == "1":
+            return "prefill_ckpt"
+        return "prefill_gated" if m and m.group(1) == "1" else "prefill"
     for key in ("kda_decode_kernel", "kda_spec_kernel", "kda_seg_scan_kernel",
-                "kda_seg_correct_kernel"):
+                "kda_seg_correct_kernel", "kda_bwd_sweep", "kda_bwd_finish"):
         if key in name:
             return key.replace("kda_", "").replace("_kernel", "")
     return None
 
 
-def source_hash() -> str:
-    """sha256 (16 hex digits) over every kernel source of the library."""
+# the source file that defines each kernel class (every kernel also
+# includes the shared device and launch headers)
+KERNEL_SOURCE = {"prefill": "kda_prefill.hip", "prefill_gated": "kda_prefill.hip",
+                 "prefill_ckpt": "kda_prefill.hip",
+                 "seg_scan": "kda_prefill.hip", "seg_correct": "kda_prefill.hip",
+                 "decode": "kda_decode.hip", "spec": "kda_spec.hip",
+                 "bwd_sweep": "kda_backward.hip", "bwd_finish": "kda_backward.hip"}
+SHARED_HEADERS = ("kda_device.h", "kda_launch.h")
+
+
+def source_hash(cls: str) -> str:
+    """sha256 (16 hex digits) over the sources kernel class `cls` is built
+    from: its defining file and the shared headers."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if p.endswith((".hip", ".h", ".cpp")):
-            with open(p, "rb") as f:
-                h.update(os.path.basename(p).encode())
-                h.update(f.read())
+    for name in (KERNEL_SOURCE[cls],) + SHARED_HEADERS:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -119,14 +134,14 @@ def pmc(out_json, workload, copy_mib, commands, fetch_dir, write_dir, sq_dir=Non
     if "copy" not in fe or "copy" not in wr:
         raise SystemExit("the calibration copy is missing from the counter output")
     rf, rw = copy_bytes / (fe["copy"] * 1024), copy_bytes / (wr["copy"] * 1024)
-    rec = {"workload": workload, "kernel_source_sha256_16": source_hash(),
+    rec = {"workload": workload,
            "copy_bytes": copy_bytes, "copy_fetch_raw": fe["copy"] * 1024,
            "copy_write_raw": wr["copy"] * 1024, "fetch_scale": rf, "write_scale": rw,
            "commands": commands, "kernels": {}}
     for cls in sorted(set(fe) | set(wr)):
         if cls == "copy":
             continue
-        k = rec["kernels"].setdefault(cls, {})
+        k = rec["kernels"].setdefault(cls, {"source_sha256_16": source_hash(cls)})
         if cls in fe:
             k["fetch_bytes"] = fe[cls] * 1024 * rf
         if cls in wr:
@@ -140,7 +155,7 @@ def pmc(out_json, workload, copy_mib, commands, fetch_dir, write_dir, sq_dir=Non
             if cls == "copy":
                 continue
             gui = per["GRBM_GUI_ACTIVE"][cls]
-            k = rec["kernels"].setdefault(cls, {})
+            k = rec["kernels"].setdefault(cls, {"source_sha256_16": source_hash(cls)})
             raw = {name: per[name].get(cls) for name in SQ_COUNTERS}
             k["sq_raw"] = raw
             # rocprofv3's derived metrics: MfmaUtil, VALUBusy, LDSBankConflict

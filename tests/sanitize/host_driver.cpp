@@ -176,7 +176,8 @@ int main()
                                gk.data(), gv.data(), gg.data(), gb.data(), nullptr, wsp, need,
                                nullptr) == KDA_OK);
         EXPECT(kda::g_prefill_calls == pf + 1 && kda::g_last_prefill.ckpt != nullptr &&
-               kda::g_last_prefill.skip_o && kda::g_bwd_calls == 1);
+               kda::g_last_prefill.o == nullptr && !kda::g_last_prefill.gated &&
+               kda::g_bwd_calls == 1);
         EXPECT(kda_bwd_chunked(q.data(), k.data(), v.data(), g.data(), beta.data(), nullptr,
                                nullptr, 1, N, H, D, D, KDA_BF16, o.data(), nullptr, gq.data(),
                                gq.data(), gv.data(), gg.data(), gb.data(), nullptr, wsp, need,

@@ -222,3 +222,11 @@ def test_bwd_validation(lib):
     assert call(a13=None) == 1 and "dO is NULL" in _lib.last_error()
     assert call(a15=P) == 1 and "overlaps" in _lib.last_error()
     assert call(a7=0, a8=0) == 0
+
+
+def test_binding_exports_every_name():
+    """Every name the Python binding lists exists (bench.py and the tests
+    call them by these names)."""
+    import gated_delta_rule_95_amd as m
+    for name in m.__all__:
+        assert callable(getattr(m, name)), name

@@ -44,12 +44,14 @@ def record(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
     import profile_summary
 
-    def write(file_workload="prefill", **kw):
+    def write(file_workload="prefill", prefill_hash=None, **kw):
+        h = profile_summary.source_hash
         rec = {"workload": file_workload,
-               "kernel_source_sha256_16": profile_summary.source_hash(),
-               "kernels": {"prefill": {"hbm_bytes_per_dispatch": 123.0, "mfma_busy_pct": 30.0,
+               "kernels": {"prefill": {"source_sha256_16": prefill_hash or h("prefill"),
+                                       "hbm_bytes_per_dispatch": 123.0, "mfma_busy_pct": 30.0,
                                        "valu_busy_pct": 40.0},
-                           "decode": {"hbm_bytes_per_dispatch": 7.0}}}
+                           "decode": {"source_sha256_16": h("decode"),
+                                      "hbm_bytes_per_dispatch": 7.0}}}
         rec.update(kw)
         (tmp_path / f"pmc_{file_workload}.json").write_text(json.dumps(rec))
     return write
@@ -63,9 +65,11 @@ def test_counters_only_for_matching_source_workload_and_kernel(record):
     assert bench.attach_counters({}, "prefill", "spec") == {"traffic": None}
     # counters taken on the prefill workload say nothing about other workloads
     assert bench.attach_counters({}, "long_prefill", "prefill") == {"traffic": None}
-    # a record taken on other kernel sources is stale
-    record(kernel_source_sha256_16="0" * 16)
+    # a kernel's figures taken on other sources of that kernel are stale;
+    # the other kernels' figures in the same record still count
+    record(prefill_hash="0" * 16)
     assert bench.attach_counters({}, "prefill", "prefill") == {"traffic": None}
+    assert bench.attach_counters({}, "prefill", "decode") == {"traffic": 7.0}
     # a record filed under another workload's name is not trusted
     record(workload="varlen")
     assert bench.counter_record("prefill", "prefill") is None
@@ -78,9 +82,18 @@ def test_counters_missing_record(tmp_path, monkeypatch):
 
 def test_kernel_classes():
     import profile_summary as ps
-    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb0EEEvNS_6"
+    # every class has a defining source, and its hash depends on that file only
+    for cls in ps.KERNEL_SOURCE:
+        assert len(ps.source_hash(cls)) == 16
+    assert ps.source_hash("prefill") == ps.source_hash("seg_scan")
+    assert ps.source_hash("prefill") != ps.source_hash("bwd_sweep")
+    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb0ELb0EEEvNS_6"
                            "ParamsIT_T0_EE") == "prefill"
-    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb1EEEvNS_6"
+    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb1ELb0EEEvNS_6"
                            "ParamsIT_T0_EE") == "prefill_gated"
+    assert ps.kernel_class("_ZN3kda18kda_prefill_kernelIDF16bDF16bLi128ELi128ELi4ELi3ELb0ELb1EEEvNS_6"
+                           "ParamsIT_T0_EE") == "prefill_ckpt"
     assert ps.kernel_class("void kda::kda_seg_scan_kernel<128, 128>(float const*)") == "seg_scan"
     assert ps.kernel_class("__amd_rocclr_copyBuffer") == "copy"
+    assert ps.kernel_class("void kda::kda_bwd_sweep<__hip_bfloat16, 128, 128, 64>(kda::SweepArgs)") == "bwd_sweep"
+    assert ps.kernel_class("void kda::kda_bwd_finish<__hip_bfloat16, 128, 128>(kda::FinishArgs)") == "bwd_finish"
