@@ -465,11 +465,13 @@ KDA_API kda_status kda_bwd_chunked(const void *q, const void *k, const void *v, 
                     workspace_bytes, need);
     const bool tok = n_tokens > 0;
     const size_t in_b = in_dtype == KDA_BF16 ? 2 : 4;
-    const Ptr ps[] = {{q, "q", tok, in_b}, {k, "k", tok, in_b}, {v, "v", tok, in_b},
-                      {g, "g", tok, 4}, {beta, "beta", tok, 4}, {dO, "dO", tok, in_b},
-                      {S0, "S0", false, 4}, {dS_T, "dS_T", false, 4}, {dq, "dq", tok, 4},
-                      {dk, "dk", tok, 4}, {dv, "dv", tok, 4}, {dg, "dg", tok, 4},
-                      {dbeta, "dbeta", tok, 4}, {dS0, "dS0", false, 4}};
+    // alignment: the widest vector access the kernels make
+    const Ptr ps[] = {{q, "q", tok, 2 * in_b}, {k, "k", tok, 2 * in_b},
+                      {v, "v", tok, 4 * in_b}, {g, "g", tok, 8}, {beta, "beta", tok, 4},
+                      {dO, "dO", tok, 4 * in_b}, {S0, "S0", false, 4},
+                      {dS_T, "dS_T", false, 4}, {dq, "dq", tok, 16}, {dk, "dk", tok, 16},
+                      {dv, "dv", tok, 4}, {dg, "dg", tok, 4}, {dbeta, "dbeta", tok, 4},
+                      {dS0, "dS0", false, 4}};
     if ((s = check_ptrs(ps, 14)) != KDA_OK) return s;
     const size_t nk = (size_t)n_tokens * H * d_k, nv = (size_t)n_tokens * H * d_v;
     const size_t st = (size_t)n_seqs * H * d_k * d_v * 4;

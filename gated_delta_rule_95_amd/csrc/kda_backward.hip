@@ -25,17 +25,25 @@
 //
 // The carried cotangent L only meets products that contract over d_k or
 // over the 16 tokens, so its columns split into blocks as the forward's
-// state does: kda_bwd_sweep runs one workgroup per (sequence, head, block of
-// columns) backwards over the chunks, from the chunk-start states that the
-// prefill kernel checkpointed, and writes its dv and dS0 columns directly.
-// The products that contract over d_v (dO Sd^T, dX Sd^T, U L^T, dU X^T,
-// dO U^T, dgamma) only feed the per-chunk gradients; every block writes its
-// partial sums, and kda_bwd_finish, one workgroup per (chunk, head), adds
-// them up and forms dq, dk, dg and dbeta, all chunks in parallel.
+// state does; the products that contract over d_v (dO Sd^T, dX Sd^T,
+// U L^T, dU X^T, dO U^T, dgamma) only feed the per-chunk gradients.  Two
+// implementations:
 //
-// Arithmetic is fp32 on the vector ALU throughout (no matrix cores, no
-// bf16 operands); products are LDS-staged, each thread accumulating a small
-// tile of outputs.
+//  * bf16 inputs, d_k >= 32 (the matrix-core path, second half of this
+//    file): kda_bwd_sweep_mfma carries L through the chunks in reverse and
+//    writes dv, dS0 and every chunk's exit cotangent; kda_bwd_chunk then
+//    forms all of a chunk's remaining gradients from its checkpointed
+//    entry state and exit cotangent, every (chunk, head) in parallel.
+//  * fp32 inputs (the precision reference) and d_k = 16 (first half):
+//    kda_bwd_sweep runs one workgroup per (sequence, head, block of
+//    columns) backwards over the chunks and writes dv, dS0 and per-block
+//    partial sums of the d_v-contracted products; kda_bwd_finish, one
+//    workgroup per (chunk, head), adds them up and forms dq, dk, dg and
+//    dbeta.  Arithmetic is fp32 on the vector ALU (LDS-staged products,
+//    each thread accumulating a small tile of outputs).
+#include <cstddef>
+
+#include "kda_chunk.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -472,6 +480,661 @@ void kda_bwd_finish(const TI *__restrict__ q, const TI *__restrict__ k,
     if (tid < nt) db[(tok0 + tid) * H + h] = sm.db[tid];
 }
 
+// ===========================================================================
+// Matrix-core backward (bf16 inputs, d_k >= 32)
+//
+// The carried cotangent runs the chain
+//     dU = P^T dO + Kd L,   dX = T^T dU,   L <- Diag(gamma) (L + QE^T dO - KE^T dX)
+// which has the shape of the forward's state chain (a 16 x d_k by d_k x BV
+// product, a 16-token triangular product, a rank-16 update of the carried
+// d_k x BV block), so kda_bwd_sweep_mfma keeps the forward kernel's
+// organisation: per (sequence, head, block of BV columns) one workgroup,
+// consumer waves holding L in the accumulator layout, builder waves forming
+// the operands of chunk c + 2 in a three-slot LDS ring (now in reverse chunk
+// order and with dO in place of v), two helper waves forming T^T and P^T of
+// chunk c + 1.  Per chunk it writes dV = dX and the exit cotangent L of the
+// chunk (in the 16 x 16 tiles of the state checkpoints); after chunk 0, dS0.
+//
+// kda_bwd_chunk then takes every (chunk, head) independently: from the
+// chunk-start state S and the exit cotangent L it re-forms X, U, dU and dX
+// one block of 16 value columns at a time and accumulates the products that
+// contract over the value columns (dO Sd^T, dX Sd^T, L U^T, dU X^T, dO U^T
+// and the row sums of L o Sd) on the matrix cores; the rest is 16 x 16 and
+// 16 x d_k algebra.  Tiles whose contraction runs along the value columns
+// are transposed on the matrix core (a product with the identity).
+// ===========================================================================
+namespace bwdm {
+
+template <int DK, int NW>
+using SC = Cfg<bf16, DK, NW, 3, false, MODE_SWEEP>;
+template <int DK>
+using CC = Cfg<bf16, DK, 1, 3, false, MODE_CHUNK>;
+
+struct SweepParams {
+    const bf16 *q, *k, *dO;
+    const float *g, *beta, *dST;
+    const int32_t *cu_seqlens;
+    int32_t seqlen, n_tokens, n_chains, chains8, H;
+    float *Lck, *dv, *dS0;
+};
+
+__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
+__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
+
+// B operand of the identity in the [4 hi | 4 lo] slot pairing: slot 8 kg + i
+// stands for row 4 kg + i % 4, so a product of a tile's [hi | lo] split (as
+// the A operand) with it is the transposed tile, hi + lo summed in fp32
+__device__ __forceinline__ bf16x8 eye8(int lane)
+{
+    const int n = lane & 15, kg = lane >> 4;
+    bf16x8 e;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (4 * kg + (i & 3) == n) ? (bf16)1.0f : (bf16)0.0f;
+    return e;
+}
+
+// operands of chunk c + 1 that its builders have finished, read before the
+// barrier that ends chunk c
+struct AheadB {
+    bf16x4 v;            // dO of the lane's column, tokens 4 g4 .. 4 g4 + 3
+    bf16x8 dh, dl;       // Kd hi / lo, first 32-deep step
+};
+template <class C>
+__device__ __forceinline__ void read_ahead_b(const Buf<C> &B, AheadB &a, int wave, int lane)
+{
+    const int j = lane & 15, g4 = lane >> 4;
+    a.v = ld4b(&B.VT[16 * wave + j][4 * g4]);
+    a.dh = ld8b(&B.DH[j][8 * g4]);
+    a.dl = ld8b(&B.DL[j][8 * g4]);
+}
+
+// one chunk of the cotangent chain for this wave's 16 columns; L holds rows
+// 16 t + 4 g4 + i of column j (lane (j, g4)); returns dX (lane (j, g4):
+// tokens 4 g4 + i of column j)
+template <class C>
+__device__ __forceinline__ f32x4 consume_sweep(const Buf<C> &B, f32x4 (&L)[C::DK / 16],
+                                               const AheadB &ah, int lane)
+{
+    constexpr int NS = C::DK / 32;
+    const int j = lane & 15, g4 = lane >> 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const NegEye ne = neg_eye(lane);
+    const bf16x8 dov = cat(ah.v, ah.v);
+    // T^T and P^T of the chunk are final when the chunk starts
+    const bf16x8 pt = ld8b(&B.PH[j][8 * g4]);
+    const bf16x8 tth = ld8b(&B.TH[j][8 * g4]), ttl = ld8b(&B.TL[j][8 * g4]);
+    // dU = P^T dO + Kd L: [PTh | PTl] against [dO | dO]; Kd (hi, lo) against
+    // L as a hi/lo pair, K slots in the stored channel order of Kd
+    f32x4 du = mma32(pt, dov, zero);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        bf16x8 lh, ll;
+        split8(L[2 * s], L[2 * s + 1], ne, lh, ll);
+        const int kk = 32 * s + 8 * g4;
+        const bf16x8 dh = s == 0 ? ah.dh : ld8b(&B.DH[j][kk]);
+        const bf16x8 dl = s == 0 ? ah.dl : ld8b(&B.DL[j][kk]);
+        du = mma32(dh, lh, du);
+        du = mma32(dl, lh, du);
+        du = mma32(dh, ll, du);
+    }
+    // L += QE^T dO (every read of the old L went into the splits above)
+#pragma unroll
+    for (int t = 0; t < C::DK / 16; ++t)
+        L[t] = mma32(ld8b(&B.KQ[16 * t + j][32 + 8 * g4]), dov, L[t]);
+    // dX = T^T dU: [TTh | TTh] and [TTl | TTl] against [dUh; dUl]
+    bf16x4 uh, ul;
+    split4(du, ne, uh, ul);
+    const bf16x8 duhl = cat(uh, ul);
+    f32x4 dx = mma32(tth, duhl, zero);
+    dx = mma32(ttl, duhl, dx);
+    // L += -KE^T dX, then the chunk's decay: L_prev = Diag(gamma) dSd
+    bf16x4 xh, xl;
+    split4(dx, ne, xh, xl);
+    const bf16x8 bxh = cat(xh, xh), bxl = cat(xl, xl);
+#pragma unroll
+    for (int t = 0; t < C::DK / 16; ++t) {
+        const bf16x8 a = ld8b(&B.KQ[16 * t + j][8 * g4]);
+        L[t] = mma32(a, bxh, L[t]);
+        L[t] = mma32(a, bxl, L[t]);
+        L[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
+    }
+    return dx;
+}
+
+}  // namespace bwdm
+
+// One workgroup per (sequence, head, block of BV columns); chunks in reverse.
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__((bwdm::SC<DK, NW>::NT), 1)
+void kda_bwd_sweep_mfma(const bwdm::SweepParams p)
+{
+    using namespace bwdm;
+    using C = SC<DK, NW>;
+    constexpr int NB = DV / C::BV;
+    __shared__ Smem<C> sm;
+    const int H = p.H;
+    // workgroup -> job as in the prefill: the blocks of a chain share an XCD
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, rest = bid >> 3;
+    const int vb = rest % NB;
+    const int chain = (rest / NB) * 8 + xcd;
+    if (chain >= p.n_chains) return;
+    const int h = chain % H;
+    int n = chain / H;
+    if (p.cu_seqlens && p.n_chains / H <= kLptMaxSeqs)
+        n = __builtin_amdgcn_readfirstlane(
+            seq_of_rank(p.cu_seqlens, p.n_chains / H, n, threadIdx.x & 63));
+    const int64_t state_of = (int64_t)n * H + h;
+    int64_t bos, T;
+    if (p.cu_seqlens) {
+        const int32_t c0 = p.cu_seqlens[n], c1 = p.cu_seqlens[n + 1];
+        const int32_t a0 = c0 < 0 ? 0 : (c0 > p.n_tokens ? p.n_tokens : c0);
+        const int32_t a1 = c1 < 0 ? 0 : (c1 > p.n_tokens ? p.n_tokens : c1);
+        bos = a0;
+        T = a1 > a0 ? a1 - a0 : 0;
+    } else {
+        bos = (int64_t)n * p.seqlen;
+        T = p.seqlen;
+    }
+    const int col_base = vb * C::BV;
+    bos = uniform64(bos);
+    const int Tn = __builtin_amdgcn_readfirstlane((int)T);
+    const int nch = (Tn + 15) / 16;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_cons = wave < NW;
+    const bool is_build = !is_cons && wave < NW + C::NBW;
+    const int bw = wave - NW, btid = tid - C::NC;
+    const int j = lane & 15, g4 = lane >> 4;
+
+    auto ntok_of = [&](int rc) -> int {
+        const int rem = Tn - 16 * rc;
+        return rem < 0 ? 0 : (rem < 16 ? rem : 16);
+    };
+    // processing step cc takes chunk nch - 1 - cc; steps past the last
+    // chunk read nothing
+    auto chunk_of = [&](int cc) -> int { return cc < nch ? nch - 1 - cc : 0; };
+    auto ntok_step = [&](int cc) -> int { return cc < nch ? ntok_of(nch - 1 - cc) : 0; };
+    auto slot = [&](int s) -> Buf<C> & { return sm.buf[__builtin_amdgcn_readfirstlane(s)]; };
+
+    // the phase plan of the prefill kernel, over processing steps
+    if (is_build) {
+        constexpr int NR = C::NR;
+        Raw<C> r[NR];
+        auto load = [&](Raw<C> &x, int cc) {
+            load_raw<C>(x, p.q, p.k, p.dO, p.g, p.beta, bos + 16 * (int64_t)chunk_of(cc),
+                        ntok_step(cc), ntok_step(cc), H, h, DV, col_base, bw, lane, btid);
+        };
+#pragma unroll
+        for (int i = 0; i < NR; ++i) load(r[i], i);
+        if (nch > 0) build<C>(sm.buf[0], r[0], bw, lane, btid, 1.f);
+        load(r[0], NR);
+        if (nch > 1) build<C>(sm.buf[1], r[1], bw, lane, btid, 1.f);
+        load(r[1], NR + 1);
+        __syncthreads();
+        __syncthreads();
+        int c = 0;
+#pragma unroll 1
+        for (; c + NR <= nch; c += NR) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, 1.f);
+                load(r[(i + 2) % NR], c + i + 2 + NR);
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NR - 1; ++i) {
+            if (c + i < nch) {
+                if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, 1.f);
+                __syncthreads();
+            }
+        }
+    } else if (!is_cons) {
+        auto help = [&](Buf<C> &B) {
+            if (wave == NW + C::NBW) helper<C, 0>(B, lane);
+            else helper<C, 1>(B, lane);
+        };
+        __syncthreads();
+        if (nch > 0) help(sm.buf[0]);
+        __syncthreads();
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            if (c + 1 < nch) help(slot((c + 1) % 3));
+            __syncthreads();
+        }
+    } else {
+        // L[:, col_base + 16 wave + j], rows 16 t + 4 g4 + i
+        f32x4 L[DK / 16];
+        const int col = col_base + 16 * wave + j;
+#pragma unroll
+        for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                L[t][i] = p.dST ? p.dST[state_of * DK * DV + (int64_t)(16 * t + 4 * g4 + i) * DV + col]
+                                : 0.f;
+        // exit-cotangent tiles of this wave's columns, chunk 0 of the sequence
+        f32x4 *lk = reinterpret_cast<f32x4 *>(p.Lck + ((bos / 16 + n) * H + h) * (int64_t)(DK * DV)) +
+                    ((col_base / 16 + wave) * (DK / 16)) * WAVE + lane;
+        const int drow = H * DV * 4;          // bytes per token of dv (< 2^27, host)
+        __syncthreads();
+        __syncthreads();
+        AheadB ah;
+        read_ahead_b<C>(sm.buf[0], ah, wave, lane);
+#pragma unroll 1
+        for (int cc = 0; cc < nch; ++cc) {
+            const int rc = nch - 1 - cc;
+#pragma unroll
+            for (int t = 0; t < DK / 16; ++t) lk[(int64_t)rc * H * (DK * DV / 4) + t * WAVE] = L[t];
+            const f32x4 dx = consume_sweep<C>(slot(cc % 3), L, ah, lane);
+            const rsrc_t rd = make_rsrc(p.dv + (bos + 16 * (int64_t)rc) * H * DV, ntok_of(rc) * drow);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bstore(rd, (4 * g4 + i) * drow + (h * DV + col) * 4, dx[i]);
+            read_ahead_b<C>(slot((cc + 1) % 3), ah, wave, lane);
+            __syncthreads();
+        }
+        if (p.dS0) {
+#pragma unroll
+            for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.dS0[state_of * DK * DV + (int64_t)(16 * t + 4 * g4 + i) * DV + col] = L[t][i];
+        }
+    }
+}
+
+namespace bwdm {
+
+struct ChunkParams {
+    const bf16 *q, *k, *v, *dO;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    int32_t n_seqs, seqlen, n_tokens, H;
+    const float *Sck, *Lck;
+    float *dq, *dk, *dg, *db;
+};
+
+template <int DK, int DV>
+struct ChunkSmem {
+    Buf<CC<DK>> b;
+    // the column-contracted sums in [channel x token] accumulator tiles
+    // (lane (token n, g4) of tile t: channels 16 t + 4 g4 + e):
+    // [0] Sd dO^T, [1] Sd dX^T, [2] L U^T
+    alignas(16) f32x4 RED[3][DK / 16][WAVE];
+    alignas(16) f32x4 RT[2][WAVE];       // dU X^T, dO U^T (lane (i, g4): rows 4 g4 + e)
+    alignas(16) float DT[16][17], DP[16][17], DM[16][17], W[16][17], DA[16][17];
+    alignas(16) float RG[DK];            // sum over the columns of L o Sd
+    alignas(16) float GQ[DK];            // sum over the tokens of QE o (dO Sd^T) - KE o (dX Sd^T)
+    alignas(16) float DB[16];
+};
+
+}  // namespace bwdm
+
+// One workgroup (four waves) per (chunk slot, head); sized for two
+// workgroups per compute unit.
+template <int DK, int DV>
+__global__ __launch_bounds__(256, 2)
+void kda_bwd_chunk(const bwdm::ChunkParams p)
+{
+    using namespace bwdm;
+    using C = CC<DK>;
+    constexpr int NT16 = DK / 16, NS = DK / 32;
+    __shared__ ChunkSmem<DK, DV> sm;
+    Buf<C> &B = sm.b;
+    // the log-decay terms dx [token][channel] reuse the -KE and QE hi rows,
+    // which nothing reads after the column blocks
+    static_assert(sizeof(float) * 16 * (DK + 4) <= sizeof(B.NK) + sizeof(B.QH), "dx scratch");
+    static_assert(offsetof(Buf<C>, QH) == offsetof(Buf<C>, NK) + sizeof(B.NK), "dx scratch");
+    float (*DXS)[DK + 4] = reinterpret_cast<float (*)[DK + 4]>(&B.NK[0][0]);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, g4 = lane >> 4;
+    const int H = p.H;
+    const int64_t slot = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    // the slot's sequence: chunk c of sequence n has slot bos_n / 16 + n + c
+    auto bos_of = [&](int s) -> int64_t {
+        if (!p.cu_seqlens) return (int64_t)s * p.seqlen;
+        const int32_t c0 = p.cu_seqlens[s];
+        return c0 < 0 ? 0 : (c0 > p.n_tokens ? p.n_tokens : c0);
+    };
+    int lo = 0, hi = p.n_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (bos_of(mid) / 16 + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t bos = bos_of(n);
+    int64_t T;
+    if (p.cu_seqlens) {
+        const int32_t c1 = p.cu_seqlens[n + 1];
+        const int64_t a1 = c1 < 0 ? 0 : (c1 > p.n_tokens ? p.n_tokens : c1);
+        T = a1 > bos ? a1 - bos : 0;
+    } else {
+        T = p.seqlen;
+    }
+    const int64_t c = slot - (bos / 16 + n);
+    if (c < 0 || c * 16 >= T) return;
+    const int64_t tok0 = uniform64(bos + c * 16);
+    const int nt = __builtin_amdgcn_readfirstlane((int)(T - c * 16 < 16 ? T - c * 16 : 16));
+    // q, k, v, dO of the chunk, rows past its end read as zero
+    const int krow = H * DK * 2, vrow = H * DV * 2;      // bytes per token (< 2^27, host)
+    const rsrc_t rq = make_rsrc(p.q + tok0 * H * DK, nt * krow);
+    const rsrc_t rk = make_rsrc(p.k + tok0 * H * DK, nt * krow);
+    const rsrc_t rv = make_rsrc(p.v + tok0 * H * DV, nt * vrow);
+    const rsrc_t ro = make_rsrc(p.dO + tok0 * H * DV, nt * vrow);
+
+    // 1. chunk operands (builder waves); sums cleared
+    if (wave < C::NBW) {
+        Raw<C> r;
+        load_raw<C>(r, p.q, p.k, p.v, p.g, p.beta, tok0, nt, 0, H, h, DV, 0, wave, lane, tid);
+        build<C>(B, r, wave, lane, tid, 1.f);
+    }
+    for (int e = tid; e < 3 * NT16 * WAVE; e += 256) (&sm.RED[0][0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < 2 * WAVE; e += 256) (&sm.RT[0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = tid; ch < DK; ch += 256) sm.RG[ch] = 0.f;
+    __syncthreads();
+    // 2. helpers: T^T, P^T, (I + A)^{-1} and KE Kd^T
+    if (wave == 0) helper<C, 0>(B, lane);
+    else if (wave == 1) helper<C, 1>(B, lane);
+    __syncthreads();
+
+    // 3. blocks of 16 value columns, wave w taking blocks w, w + 4, ...  The
+    // sums are split in four groups of channel tiles; in round r of an
+    // iteration wave w adds its products into group (w + r) % 4 (and the
+    // wave of group 0 also adds dU X^T, dO U^T, that of group 1 the row sums
+    // of L o Sd), so no two waves touch the same sums between barriers
+    {
+        constexpr int NCB = DV / 16, NIT = (NCB + 3) / 4;
+        constexpr int TPQ = NT16 >= 4 ? NT16 / 4 : 1;   // channel tiles per group
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const NegEye ne = neg_eye(lane);
+        const bf16x8 eye = eye8(lane);
+        // T rows [Th | Th], [Tl | Tl] read out of the T^T rows
+        bf16x4 th4, tl4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            th4[e] = B.TH[4 * g4 + e][8 * (j >> 2) + (j & 3)];
+            tl4[e] = B.TL[4 * g4 + e][8 * (j >> 2) + (j & 3)];
+        }
+        const bf16x8 t2h = cat(th4, th4), t2l = cat(tl4, tl4);
+        const bf16x8 tth = ld8b(&B.TH[j][8 * g4]), ttl = ld8b(&B.TL[j][8 * g4]);
+        const bf16x8 pth = ld8b(&B.PH[j][8 * g4]);
+        const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.Sck + (slot * H + h) * (int64_t)(DK * DV));
+        const f32x4 *cl = reinterpret_cast<const f32x4 *>(p.Lck + (slot * H + h) * (int64_t)(DK * DV));
+#pragma unroll 1
+        for (int it = 0; it < NIT; ++it) {
+            const int cb = wave + 4 * it;
+            const bool active = cb < NCB;                 // uniform over the wave
+            bf16x8 sh[NS], sl[NS], lh[NS], ll[NS];
+            f32x4 GG[NT16], dT = zero, dP = zero;
+            bf16x8 doo = {}, buh = {}, bul = {}, bxh = {}, bxl = {};
+            if (active) {
+                f32x4 S[NT16], L[NT16];
+#pragma unroll
+                for (int t = 0; t < NT16; ++t) {
+                    S[t] = cs[(cb * NT16 + t) * WAVE + lane];
+                    L[t] = cl[(cb * NT16 + t) * WAVE + lane];
+                }
+                const int col = 16 * cb + j;
+                // v and dO of column col, tokens 4 g4 + i; dO of token j,
+                // columns 16 cb + 4 g4 .. + 3
+                typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+                u16x4 vb, ob;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int off = (4 * g4 + i) * vrow + (h * DV + col) * 2;
+                    vb[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
+                    ob[i] = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
+                }
+                const bf16x4 v4 = __builtin_bit_cast(bf16x4, vb), d4 = __builtin_bit_cast(bf16x4, ob);
+                const bf16x4 o4 = __builtin_bit_cast(
+                    bf16x4, bload64(ro, j * vrow + (h * DV + 16 * cb + 4 * g4) * 2));
+                doo = cat(o4, o4);
+                // Sd, and the row sums of L o Sd over this block's columns
+#pragma unroll
+                for (int t = 0; t < NT16; ++t) {
+                    S[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
+                    GG[t] = L[t] * S[t];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) GG[t][e] = group_sum<16>(GG[t][e]);
+                }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    split8(S[2 * s], S[2 * s + 1], ne, sh[s], sl[s]);
+                    split8(L[2 * s], L[2 * s + 1], ne, lh[s], ll[s]);
+                }
+                // X = V - KE Sd
+                f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const bf16x8 nk = ld8b(&B.NK[j][32 * s + 8 * g4]);
+                    x = mma32(nk, sh[s], x);
+                    x = mma32(nk, sl[s], x);
+                }
+                bf16x4 xh, xl;
+                split4(x, ne, xh, xl);
+                const bf16x8 xhl = cat(xh, xl);
+                // U = T X
+                f32x4 u = mma32(t2h, xhl, zero);
+                u = mma32(t2l, xhl, u);
+                // dU = P^T dO + Kd L
+                f32x4 du = mma32(pth, cat(d4, d4), zero);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int kk = 32 * s + 8 * g4;
+                    const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
+                    du = mma32(dh, lh[s], du);
+                    du = mma32(dl, lh[s], du);
+                    du = mma32(dh, ll[s], du);
+                }
+                bf16x4 uh, ul, duh, dul;
+                split4(u, ne, uh, ul);
+                split4(du, ne, duh, dul);
+                const bf16x8 uhl = cat(uh, ul), duhl = cat(duh, dul);
+                // dX = T^T dU
+                f32x4 dx = mma32(tth, duhl, zero);
+                dx = mma32(ttl, duhl, dx);
+                bf16x4 dxh, dxl;
+                split4(dx, ne, dxh, dxl);
+                // transposed tiles (value columns as rows): lane (token n, g4)
+                // holds columns 16 cb + 4 g4 .. + 3 of token n
+                bf16x4 xth, xtl, uth, utl, duth, dutl, dxth, dxtl;
+                split4(mma32(xhl, eye, zero), ne, xth, xtl);
+                split4(mma32(uhl, eye, zero), ne, uth, utl);
+                split4(mma32(duhl, eye, zero), ne, duth, dutl);
+                split4(mma32(cat(dxh, dxl), eye, zero), ne, dxth, dxtl);
+                // dU X^T and dO U^T (16 x 16, lane (i, g4): rows 4 g4 + e)
+                dT = mma32(cat(duth, dutl), cat(xth, xth), zero);
+                dT = mma32(cat(duth, dutl), cat(xtl, xtl), dT);
+                dP = mma32(doo, cat(uth, utl), zero);
+                buh = cat(uth, uth); bul = cat(utl, utl);
+                bxh = cat(dxth, dxth); bxl = cat(dxtl, dxtl);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int grp = (wave + r) & 3;
+                if (active) {
+#pragma unroll
+                    for (int G = 0; G < 4; ++G) {
+                        if (G != grp || G * TPQ >= NT16) continue;
+#pragma unroll
+                        for (int tt = 0; tt < TPQ; ++tt) {
+                            const int t = G * TPQ + tt, s = t >> 1;
+                            const bf16x8 shl = (t & 1) ? cat(hi4(sh[s]), hi4(sl[s]))
+                                                       : cat(lo4(sh[s]), lo4(sl[s]));
+                            const bf16x8 lhl = (t & 1) ? cat(hi4(lh[s]), hi4(ll[s]))
+                                                       : cat(lo4(lh[s]), lo4(ll[s]));
+                            bf16x4 sth, stl, lth, ltl;
+                            split4(mma32(shl, eye, zero), ne, sth, stl);   // Sd tile t transposed
+                            split4(mma32(lhl, eye, zero), ne, lth, ltl);   // L tile t transposed
+                            const bf16x8 sa = cat(sth, stl), la = cat(lth, ltl);
+                            f32x4 y1 = sm.RED[0][t][lane], y2 = sm.RED[1][t][lane];
+                            f32x4 kd = sm.RED[2][t][lane];
+                            y1 = mma32(sa, doo, y1);                       // Sd dO^T
+                            y2 = mma32(sa, bxh, y2);                       // Sd dX^T
+                            y2 = mma32(sa, bxl, y2);
+                            kd = mma32(la, buh, kd);                       // L U^T
+                            kd = mma32(la, bul, kd);
+                            sm.RED[0][t][lane] = y1;
+                            sm.RED[1][t][lane] = y2;
+                            sm.RED[2][t][lane] = kd;
+                        }
+                    }
+                    if (grp == 0) {
+                        sm.RT[0][lane] += dT;
+                        sm.RT[1][lane] += dP;
+                    } else if (grp == 1 && j == 0) {
+#pragma unroll
+                        for (int t = 0; t < NT16; ++t)
+                            *reinterpret_cast<f32x4 *>(&sm.RG[16 * t + 4 * g4]) += GG[t];
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    // 4. through T = M Diag(beta) and A = strict_lower(Diag(beta) KE Kd^T)
+    const int r16 = tid >> 4, i16 = tid & 15;
+    if (tid < 64) {
+        const f32x4 a = sm.RT[0][tid], b = sm.RT[1][tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sm.DT[4 * g4 + e][j] = a[e];
+            sm.DP[4 * g4 + e][j] = b[e];
+        }
+    }
+    __syncthreads();
+    sm.DM[r16][i16] = sm.DT[r16][i16] * B.BETA[i16];                 // dM = dT Diag(beta)
+    __syncthreads();
+    {
+        float w = 0.f;                                                // W = M^T dM
+#pragma unroll
+        for (int q = 0; q < 16; ++q) w = __builtin_fmaf(B.MI[q][r16], sm.DM[q][i16], w);
+        sm.W[r16][i16] = w;
+    }
+    __syncthreads();
+    {
+        float a = 0.f;                                                // dA = -W M^T
+#pragma unroll
+        for (int q = 0; q < 16; ++q) a = __builtin_fmaf(sm.W[r16][q], B.MI[i16][q], a);
+        sm.DA[r16][i16] = i16 < r16 ? -a : 0.f;
+    }
+    __syncthreads();
+    if (tid < 16) {
+        float b = 0.f;
+        for (int q = 0; q < 16; ++q) b = __builtin_fmaf(sm.DT[q][tid], B.MI[q][tid], b);
+        for (int q = 0; q < 16; ++q) b = __builtin_fmaf(sm.DA[tid][q], B.KK[tid][q], b);
+        sm.DB[tid] = b;
+    }
+    __syncthreads();
+    sm.DA[r16][i16] *= B.BETA[r16];                                   // Diag(beta) dA
+    if (i16 > r16) sm.DP[r16][i16] = 0.f;                             // P lower incl.
+    __syncthreads();
+    // 5. dQE, dKE, dKd as [channel x token] tiles (fp32 matrix cores), then
+    // dq, dk and the log-decay terms; QE, KE, Kd are re-formed from q, k and
+    // the exponents
+    for (int t = wave; t < NT16; t += 4) {
+        f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, q2 = q1, q3 = q1;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int kk = 4 * st + g4;                               // token index i
+            const int ch = 16 * t + j;
+            const int off = kk * krow + (h * DK + ch) * 2;
+            const float qv = u16_to_f(__builtin_amdgcn_raw_buffer_load_b16(rq, off, 0, 0));
+            const float kv = u16_to_f(__builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, 0));
+            const float x = B.GX[kk][ch];
+            const float E = fast_exp2(x), F = fast_exp2(-x);
+            q1 = mma4(kv * F, sm.DP[j][kk], q1);                      // Kd^T dP^T
+            q2 = mma4(kv * F, sm.DA[j][kk], q2);                      // Kd^T dA^T
+            q3 = mma4(qv * E, sm.DP[kk][j], q3);                      // QE^T dP
+            q3 = mma4(kv * E, sm.DA[kk][j], q3);                      // + KE^T dA
+        }
+        const int off = j * krow + (h * DK + 16 * t + 4 * g4) * 2;
+        const bf16x4 q4 = __builtin_bit_cast(bf16x4, bload64(rq, off));
+        const bf16x4 k4 = __builtin_bit_cast(bf16x4, bload64(rk, off));
+        f32x4 dqv, dkv, gqv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ch = 16 * t + 4 * g4 + e;
+            const float y1 = sm.RED[0][t][lane][e], y2 = sm.RED[1][t][lane][e];
+            const float dqe = y1 + q1[e];
+            const float dke = -y2 + q2[e];
+            const float dkd = sm.RED[2][t][lane][e] + q3[e];
+            const float x = B.GX[j][ch];                              // log2 units, >= 0
+            const float E = fast_exp2(x), F = fast_exp2(-x);
+            const float qe = (float)q4[e] * E, ke = (float)k4[e] * E, kd = (float)k4[e] * F;
+            dqv[e] = dqe * E;
+            dkv[e] = dke * E + dkd * F;
+            gqv[e] = qe * y1 - ke * y2;
+            DXS[j][ch] = dqe * qe + dke * ke - dkd * kd;
+        }
+        if (j < nt) {
+            const int64_t o = ((tok0 + j) * H + h) * DK + 16 * t + 4 * g4;
+            *reinterpret_cast<f32x4 *>(p.dq + o) = dqv;
+            *reinterpret_cast<f32x4 *>(p.dk + o) = dkv;
+        }
+        // sums over the 16 tokens (the lanes of a row)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gqv[e] = group_sum<16>(gqv[e]);
+        if (j == 0) *reinterpret_cast<f32x4 *>(&sm.GQ[16 * t + 4 * g4]) = gqv;
+    }
+    __syncthreads();
+    // 6. dg: x_r = Gc_r - Gc_16 gives dGc_r = dx_r (r < 15) and the chunk
+    // total dGc_16 = gamma dgamma - sum_{r < 15} dx_r; dg_s = sum_{r >= s} dGc_r,
+    // with gamma dgamma = sum_j dSd o Sd = L o Sd + QE o (dO Sd^T) - KE o (dX Sd^T)
+    for (int ch = tid; ch < DK; ch += 256) {
+        float tot = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot += DXS[r][ch];
+        float acc = sm.RG[ch] + sm.GQ[ch] - tot + DXS[15][ch];
+        for (int r = 15; r >= 0; --r) {
+            if (r < 15) acc += DXS[r][ch];
+            if (r < nt) p.dg[((tok0 + r) * H + h) * DK + ch] = acc;
+        }
+    }
+    if (tid < nt) p.db[(tok0 + tid) * H + h] = sm.DB[tid];
+}
+
+template <int DK, int DV>
+static hipError_t launch_bwd_mfma_t(const BwdArgs &a)
+{
+    using namespace bwdm;
+    constexpr int NW = DV / 16 < 4 ? (DV / 16 < DK / 16 ? DV / 16 : DK / 16)
+                                   : (4 < DK / 16 ? 4 : DK / 16);
+    using SCf = SC<DK, NW>;
+    constexpr int NB = DV / SCf::BV;
+    static_assert(sizeof(Smem<SCf>) <= 160 * 1024, "sweep LDS");
+    static_assert(sizeof(ChunkSmem<DK, DV>) <= 160 * 1024, "chunk LDS");
+    const int64_t chains = (int64_t)a.n_seqs * a.H;
+    if (chains == 0) return hipSuccess;
+    hipStream_t st = (hipStream_t)a.stream;
+    SweepParams sp{};
+    sp.q = (const bf16 *)a.q; sp.k = (const bf16 *)a.k; sp.dO = (const bf16 *)a.dO;
+    sp.g = a.g; sp.beta = a.beta; sp.dST = a.dST; sp.cu_seqlens = a.cu_seqlens;
+    sp.seqlen = a.seqlen; sp.n_tokens = (int32_t)a.n_tokens;
+    sp.n_chains = (int32_t)chains; sp.chains8 = (int32_t)(((chains + 7) / 8) * 8); sp.H = a.H;
+    sp.Lck = a.part; sp.dv = a.dv; sp.dS0 = a.dS0;
+    const int64_t grid = (int64_t)sp.chains8 * NB;
+    hipLaunchKernelGGL((kda_bwd_sweep_mfma<DK, DV, NW>), dim3((unsigned)grid), dim3(SCf::NT), 0,
+                       st, sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t g2 = a.n_slots * a.H;
+    if (g2 == 0) return hipSuccess;
+    ChunkParams cp{};
+    cp.q = (const bf16 *)a.q; cp.k = (const bf16 *)a.k; cp.v = (const bf16 *)a.v;
+    cp.dO = (const bf16 *)a.dO; cp.g = a.g; cp.beta = a.beta; cp.cu_seqlens = a.cu_seqlens;
+    cp.n_seqs = a.n_seqs; cp.seqlen = a.seqlen; cp.n_tokens = (int32_t)a.n_tokens; cp.H = a.H;
+    cp.Sck = a.ckpt; cp.Lck = a.part;
+    cp.dq = a.dq; cp.dk = a.dk; cp.dg = a.dg; cp.db = a.dbeta;
+    hipLaunchKernelGGL((kda_bwd_chunk<DK, DV>), dim3((unsigned)g2), dim3(256), 0, st, cp);
+    return hipGetLastError();
+}
+
 template <typename TI, int DK, int DV>
 static hipError_t launch_bwd_t(const BwdArgs &a)
 {
@@ -498,9 +1161,13 @@ static hipError_t launch_bwd_t(const BwdArgs &a)
 
 size_t bwd_part_floats(int32_t d_k, int32_t d_v)
 {
+    // vector-ALU path: per-block partial sums; matrix-core path: the exit
+    // cotangent of the chunk (d_k x d_v)
     const int BV = d_v >= 64 ? 64 : d_v;
     const int NB = d_v / BV;
-    return (size_t)NB * (3 * bwd::C * d_k + 2 * bwd::C * bwd::C + d_k);
+    const size_t part = (size_t)NB * (3 * bwd::C * d_k + 2 * bwd::C * bwd::C + d_k);
+    const size_t lck = (size_t)d_k * d_v;
+    return part > lck ? part : lck;
 }
 
 template <typename TI>
@@ -516,8 +1183,22 @@ static hipError_t dispatch_bwd(const BwdArgs &a)
     return hipErrorInvalidValue;
 }
 
+static hipError_t dispatch_bwd_mfma(const BwdArgs &a)
+{
+#define KDA_BWD_CASE(DK_, DV_) \
+    if (a.d_k == DK_ && a.d_v == DV_) return launch_bwd_mfma_t<DK_, DV_>(a);
+    KDA_BWD_CASE(32, 16) KDA_BWD_CASE(32, 32) KDA_BWD_CASE(32, 64) KDA_BWD_CASE(32, 128)
+    KDA_BWD_CASE(64, 16) KDA_BWD_CASE(64, 32) KDA_BWD_CASE(64, 64) KDA_BWD_CASE(64, 128)
+    KDA_BWD_CASE(128, 16) KDA_BWD_CASE(128, 32) KDA_BWD_CASE(128, 64) KDA_BWD_CASE(128, 128)
+#undef KDA_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+// bf16 inputs with d_k >= 32 take the matrix-core kernels; fp32 inputs (the
+// precision reference) and d_k = 16 the vector-ALU ones
 hipError_t launch_bwd(const BwdArgs &a)
 {
+    if (a.in_bf16 && a.d_k >= 32) return dispatch_bwd_mfma(a);
     return a.in_bf16 ? dispatch_bwd<bf16>(a) : dispatch_bwd<float>(a);
 }
 

@@ -313,12 +313,17 @@ kda_status kda_decode_spec(const void *k_prev, const void *v_prev, const float *
  *
  * It reruns the forward keeping the state at every 16-token chunk start,
  * then walks the chunks backwards carrying the cotangent of the state, by
- * blocks of state columns, and finishes each chunk's dq, dk, dg and dbeta in
- * a second, chunk-parallel pass.  Arithmetic is fp32 throughout.  The
- * workspace (required) must hold kda_bwd_workspace_bytes(...) bytes, 256-byte
- * aligned: the checkpoints (64 KiB per chunk and head at d = 128) and the
- * blocks' partial sums.  Other arguments, layouts and errors as for
- * kda_fwd_chunked.
+ * blocks of state columns (writing dv and dS0), and forms each chunk's dq,
+ * dk, dg and dbeta in a second, chunk-parallel pass.  bf16 inputs with
+ * d_k >= 32 run on the matrix cores (bf16 hi/lo operand pairs, fp32
+ * accumulation); fp32 inputs and d_k = 16 run in fp32 on the vector ALU.
+ * The workspace (required) must hold kda_bwd_workspace_bytes(...) bytes,
+ * 256-byte aligned: the state checkpoints (64 KiB per chunk and head at
+ * d = 128) and as much again for the chunk-exit cotangents (or the column
+ * blocks' partial sums).  Pointers must be aligned to the widest access
+ * made on them: q, k to 2 elements, v, dO to 4 elements, g to 8 bytes, dq
+ * and dk to 16 bytes, the rest to 4 bytes.  Other arguments, layouts and
+ * errors as for kda_fwd_chunked.
  */
 size_t kda_bwd_workspace_bytes(int32_t n_seqs, int64_t n_tokens, int32_t H, int32_t d_k,
                                int32_t d_v);
