@@ -45,27 +45,30 @@ def kernel_class(name: str):
             return "prefill_ckpt"
         return "prefill_gated" if m and m.group(1) == "1" else "prefill"
     for key in ("kda_decode_kernel", "kda_spec_kernel", "kda_seg_scan_kernel",
-                "kda_seg_correct_kernel", "kda_bwd_sweep", "kda_bwd_finish"):
+                "kda_seg_correct_kernel", "kda_bwd_sweep_mfma", "kda_bwd_sweep",
+                "kda_bwd_finish", "kda_bwd_chunk"):
         if key in name:
             return key.replace("kda_", "").replace("_kernel", "")
     return None
 
 
-# the source file that defines each kernel class (every kernel also
-# includes the shared device and launch headers)
-KERNEL_SOURCE = {"prefill": "kda_prefill.hip", "prefill_gated": "kda_prefill.hip",
-                 "prefill_ckpt": "kda_prefill.hip",
-                 "seg_scan": "kda_prefill.hip", "seg_correct": "kda_prefill.hip",
-                 "decode": "kda_decode.hip", "spec": "kda_spec.hip",
-                 "bwd_sweep": "kda_backward.hip", "bwd_finish": "kda_backward.hip"}
+# the sources each kernel class is built from (every kernel also includes
+# the shared device and launch headers)
+_PF = ("kda_prefill.hip", "kda_chunk.h")
+_BW = ("kda_backward.hip", "kda_chunk.h")
+KERNEL_SOURCE = {"prefill": _PF, "prefill_gated": _PF, "prefill_ckpt": _PF,
+                 "seg_scan": _PF, "seg_correct": _PF,
+                 "decode": ("kda_decode.hip",), "spec": ("kda_spec.hip",),
+                 "bwd_sweep": _BW, "bwd_finish": _BW, "bwd_sweep_mfma": _BW,
+                 "bwd_chunk": _BW}
 SHARED_HEADERS = ("kda_device.h", "kda_launch.h")
 
 
 def source_hash(cls: str) -> str:
     """sha256 (16 hex digits) over the sources kernel class `cls` is built
-    from: its defining file and the shared headers."""
+    from: its own files and the shared headers."""
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCE[cls],) + SHARED_HEADERS:
+    for name in KERNEL_SOURCE[cls] + SHARED_HEADERS:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())

@@ -96,4 +96,6 @@ def test_kernel_classes():
     assert ps.kernel_class("void kda::kda_seg_scan_kernel<128, 128>(float const*)") == "seg_scan"
     assert ps.kernel_class("__amd_rocclr_copyBuffer") == "copy"
     assert ps.kernel_class("void kda::kda_bwd_sweep<__hip_bfloat16, 128, 128, 64>(kda::SweepArgs)") == "bwd_sweep"
+    assert ps.kernel_class("void kda::kda_bwd_sweep_mfma<128, 128, 4>(kda::bwdm::SweepParams)") == "bwd_sweep_mfma"
+    assert ps.kernel_class("void kda::kda_bwd_chunk<128, 128>(kda::bwdm::ChunkParams)") == "bwd_chunk"
     assert ps.kernel_class("void kda::kda_bwd_finish<__hip_bfloat16, 128, 128>(kda::FinishArgs)") == "bwd_finish"
