@@ -174,7 +174,12 @@ struct Cfg {
     static constexpr int NBW = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
-    static constexpr int NT = (NW + NBW + 2) * WAVE;   // consumers, builders, 2 helpers
+    // two auxiliary waves take the value block and the Kd^T rows off the
+    // builders (forward layouts, bf16, d_k = 128 with four consumers: with
+    // them every SIMD holds one consumer, one builder and one helper or
+    // auxiliary wave, three waves as before)
+    static constexpr bool AUX = BF && MODE_ == MODE_FWD && DK_ == 128 && NW_ == 4;
+    static constexpr int NT = (NW + NBW + 2 + (AUX ? 2 : 0)) * WAVE;   // + 2 helpers
     static constexpr int NC = NW * WAVE;           // consumer threads
     static constexpr int NVT = 4 * BV;             // builder threads that move v (4 tokens each)
     static_assert(NVT <= NBW * WAVE && NVT % WAVE == 0, "value block mapping");
@@ -335,6 +340,7 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
     // v: thread (column c, token quad tq) < NVT loads tokens 4 tq .. 4 tq + 3
     // of column c (a wave's loads of one token are consecutive columns); the
     // condition is uniform over each wave and absent when all builders move v
+    if constexpr (C::AUX) return;                  // the auxiliary waves move v
     if (!C::all_v(tid)) return;
     const int c = tid % C::BV, tq = tid / C::BV;
     const int ev = 4 * tq * rowv + h * DV + col_base + c;
@@ -566,6 +572,8 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         }
     } else if constexpr (C::CHUNK) {
         // the chunk kernel reads Kd from the fp32 copy
+    } else if constexpr (C::AUX) {
+        // the auxiliary waves write Kd^T from the Kd rows
     } else if constexpr (C::BF) {
         // Kd^T rows: this lane's TPG consecutive tokens of channels ch, ch + 1
         if constexpr (TPG == 2) {
@@ -607,7 +615,7 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         // v is stored in its input type (the raw bits): four tokens of one
         // column per thread, one 8- or 16-byte write
         const int c = tid % C::BV, tq = tid / C::BV;
-        if (C::all_v(tid)) {
+        if (!C::AUX && C::all_v(tid)) {
             if constexpr (C::BF) *reinterpret_cast<u32x2 *>(&B.VT[c][4 * tq]) = r.v;
             else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
         }

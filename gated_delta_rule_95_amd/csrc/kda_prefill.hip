@@ -249,6 +249,55 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
 // used across compute units of one device, the intra-device sequence-split
 // regime of the same essay's "KDA + Gated MLA" costs section, item (3).)
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// auxiliary waves (Cfg::AUX): the value block of a chunk and the Kd^T rows.
+// Aux thread a (0 .. 127) moves columns 2 (a % (BV / 2)) and the next one,
+// tokens 4 (a / (BV / 2)) .. + 3, and writes the Kd^T row of channel a.
+// ---------------------------------------------------------------------------
+struct AuxV {
+    uint32_t w[4];                       // 4 tokens x 2 bf16 columns
+};
+template <class C, typename TI>
+__device__ __forceinline__ void aux_load_v(AuxV &x, const TI *__restrict__ v, int64_t tok_base,
+                                           int ntok, int H, int h, int DV, int col_base, int a)
+{
+    static_assert(C::BV == 64 && C::DK == 128 && C::BF, "aux mapping");
+    constexpr int CP = C::BV / 2;
+    const int cp = a % CP, tq = a / CP;
+    const int rowv = H * DV;
+    const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok * rowv * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.w[i] = bload32(rv, ((4 * tq + i) * rowv + h * DV + col_base + 2 * cp) * 2);
+}
+template <class C>
+__device__ __forceinline__ void aux_write_v(Buf<C> &B, const AuxV &x, int a)
+{
+    constexpr int CP = C::BV / 2;
+    const int cp = a % CP, tq = a / CP;
+    // column 2 cp takes the low halves of the four token words, 2 cp + 1 the high
+    const uint32_t lo01 = __builtin_amdgcn_perm(x.w[1], x.w[0], 0x05040100u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(x.w[3], x.w[2], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(x.w[1], x.w[0], 0x07060302u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(x.w[3], x.w[2], 0x07060302u);
+    *reinterpret_cast<u32x2 *>(&B.VT[2 * cp][4 * tq]) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2 *>(&B.VT[2 * cp + 1][4 * tq]) = u32x2{hi01, hi23};
+}
+template <class C>
+__device__ __forceinline__ void aux_kh(Buf<C> &B, int a)
+{
+    const int kc = kpos<C>(a);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        bf16x8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = B.DH[4 * g + i][kc];
+            r[4 + i] = B.DL[4 * g + i][kc];
+        }
+        *reinterpret_cast<bf16x8 *>(&B.KH[a][8 * g]) = r;
+    }
+}
+
 template <typename TI, typename TO>
 struct Params {
     const TI *q, *k, *v;
@@ -383,6 +432,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
     // roles: consumer waves 0 .. NW-1, builder waves NW .. NW+NBW-1, two helpers
     const bool is_cons = wave < NW;
     const bool is_build = !is_cons && wave < NW + C::NBW;
+    const bool is_aux = C::AUX && wave >= NW + C::NBW + 2;
     const int bw = wave - NW, btid = tid - C::NC;     // builder wave / thread index
     const int j = lane & 15, g4 = lane >> 4;
 
@@ -405,8 +455,10 @@ void kda_prefill_kernel(const Params<TI, TO> p)
     //                 of chunk c (slot c % 3)
     // Each SIMD holds one consumer and one builder wave, so the builder's
     // VALU work fills the consumer's matrix-core and LDS waits; the two
-    // helper waves sit on SIMDs 0 and 1.  Every role runs its own loop; the
-    // role is wave-uniform.
+    // helper waves sit on SIMDs 0 and 1 and, where the configuration has
+    // them, the two auxiliary waves on SIMDs 2 and 3 (the value block on the
+    // builders' schedule, the Kd^T rows on the helpers').  Every role runs
+    // its own loop over the same barriers; the role is wave-uniform.
     static_assert(NBUF == 3 && LAG == 2, "phase plan");
     if (is_build) {
         // Loads are issued unconditionally: buffer resources of chunks past
@@ -453,6 +505,47 @@ void kda_prefill_kernel(const Params<TI, TO> p)
             if (c + i < nch) {
                 if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, ea);
                 __syncthreads();
+            }
+        }
+    } else if (is_aux) {
+        if constexpr (C::AUX) {
+            // the value block of chunk c + 2 (loads three phases ahead, like
+            // the builders') and the Kd^T rows of chunk c + 1, whose Kd rows
+            // the builders wrote a phase earlier
+            const int a = tid - (NW + C::NBW + 2) * WAVE;
+            constexpr int NR = 3;
+            AuxV r[NR];
+            auto load = [&](AuxV &x, int cc) {
+                aux_load_v<C>(x, p.v, bos + 16 * (int64_t)cc, v_on ? ntok_of(cc) : 0, H, h, DV,
+                              col_base, a);
+            };
+#pragma unroll
+            for (int i = 0; i < NR; ++i) load(r[i], i);
+            if (nch > 0) aux_write_v<C>(sm.buf[0], r[0], a);
+            load(r[0], NR);
+            if (nch > 1) aux_write_v<C>(sm.buf[1], r[1], a);
+            load(r[1], NR + 1);
+            __syncthreads();
+            if (nch > 0) aux_kh<C>(sm.buf[0], a);
+            __syncthreads();
+            int c = 0;
+#pragma unroll 1
+            for (; c + NR <= nch; c += NR) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
+                    load(r[(i + 2) % NR], c + i + 2 + NR);
+                    if (c + i + 1 < nch) aux_kh<C>(slot((c + i + 1) % 3), a);
+                    __syncthreads();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NR - 1; ++i) {
+                if (c + i < nch) {
+                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
+                    if (c + i + 1 < nch) aux_kh<C>(slot((c + i + 1) % 3), a);
+                    __syncthreads();
+                }
             }
         }
     } else if (!is_cons) {
