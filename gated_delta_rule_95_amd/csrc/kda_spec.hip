@@ -171,8 +171,11 @@ __device__ __forceinline__ void spec_token(int tid, SpecSmem<DK, DV> &sm,
     // its own first barrier, which every thread reaches after reading u
 }
 
+// A workgroup's tokens are a chain of barriers and column reductions, so two
+// workgroups per compute unit overlap each other's waits: at 1024 threads
+// that needs 8 waves per SIMD, at most 64 VGPRs (the LDS holds two).
 template <typename TI, typename TO, int DK, int DV>
-__global__ __launch_bounds__((SpecShape<DK, DV>::NT))
+__global__ __launch_bounds__((SpecShape<DK, DV>::NT), (SpecShape<DK, DV>::NT >= 1024 ? 8 : 1))
 void kda_spec_kernel(const SpecParams<TI, TO> p)
 {
     using Sh = SpecShape<DK, DV>;
