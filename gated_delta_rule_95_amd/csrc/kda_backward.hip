@@ -726,7 +726,8 @@ void kda_bwd_sweep_mfma(const bwdm::SweepParams p)
         for (int cc = 0; cc < nch; ++cc) {
             const int rc = nch - 1 - cc;
 #pragma unroll
-            for (int t = 0; t < DK / 16; ++t) lk[(int64_t)rc * H * (DK * DV / 4) + t * WAVE] = L[t];
+            for (int t = 0; t < DK / 16; ++t)   // read once, by the chunk kernel: streamed
+                __builtin_nontemporal_store(L[t], &lk[(int64_t)rc * H * (DK * DV / 4) + t * WAVE]);
             const f32x4 dx = consume_sweep<C>(slot(cc % 3), L, ah, lane);
             const rsrc_t rd = make_rsrc(p.dv + (bos + 16 * (int64_t)rc) * H * DV, ntok_of(rc) * drow);
 #pragma unroll
@@ -875,9 +876,9 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             if (active) {
                 f32x4 S[NT16], L[NT16];
 #pragma unroll
-                for (int t = 0; t < NT16; ++t) {
-                    S[t] = cs[(cb * NT16 + t) * WAVE + lane];
-                    L[t] = cl[(cb * NT16 + t) * WAVE + lane];
+                for (int t = 0; t < NT16; ++t) {       // checkpoints: read once, streamed
+                    S[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
+                    L[t] = __builtin_nontemporal_load(&cl[(cb * NT16 + t) * WAVE + lane]);
                 }
                 const int col = 16 * cb + j;
                 // v and dO of column col, tokens 4 g4 + i; dO of token j,

@@ -600,8 +600,8 @@ void kda_prefill_kernel(const Params<TI, TO> p)
             store_o(c - 1);
             if constexpr (CKPT) {
 #pragma unroll
-                for (int t = 0; t < DK / 16; ++t)
-                    ck[(int64_t)c * H * (DK * DV / 4) + t * WAVE] = S[t];
+                for (int t = 0; t < DK / 16; ++t)   // read once, by the backward: streamed
+                    __builtin_nontemporal_store(S[t], &ck[(int64_t)c * H * (DK * DV / 4) + t * WAVE]);
             }
             ov = consume<C>(slot(c % 3), S, ah, wave, lane);
             read_ahead<C>(slot((c + 1) % 3), ah, wave, lane);
