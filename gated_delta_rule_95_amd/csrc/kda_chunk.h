@@ -448,9 +448,10 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         G0[t] = s0;
         G1[t] = s1;
     }
-    if constexpr (C::GATED) {
+    if constexpr (C::GATED && !C::AUX) {
         // partial |q|^2 and |k|^2 of this lane's tokens over the wave's
         // channels: sum the channel pairs of the CPW lanes of a token group
+        // (with auxiliary waves, they form the whole sums instead)
 #pragma unroll
         for (int t = 0; t < TPG; ++t) {
             const float qa = elem<C>(r.q[t], 0), qb = elem<C>(r.q[t], 1);
@@ -790,8 +791,9 @@ __device__ __forceinline__ void helper(Buf<C> &B, int lane)
         // Diag(s_k) T, and the consumer's products as row scales
         float nq = 0.f, nk = 0.f;
         f32x4 nk4 = {0.f, 0.f, 0.f, 0.f};
+        constexpr int NP = C::AUX ? 1 : C::NBW;      // partial sums per token
 #pragma unroll
-        for (int w = 0; w < C::NBW; ++w) {
+        for (int w = 0; w < NP; ++w) {
             nq += B.NRM[0][w][j];
             nk += B.NRM[1][w][j];
             nk4 += *reinterpret_cast<const f32x4 *>(&B.NRM[1][w][4 * g4]);

@@ -282,6 +282,47 @@ __device__ __forceinline__ void aux_write_v(Buf<C> &B, const AuxV &x, int a)
     *reinterpret_cast<u32x2 *>(&B.VT[2 * cp][4 * tq]) = u32x2{lo01, lo23};
     *reinterpret_cast<u32x2 *>(&B.VT[2 * cp + 1][4 * tq]) = u32x2{hi01, hi23};
 }
+// gated prologue: |q|^2 and |k|^2 of each token.  Aux thread a takes
+// token a / 8 and channels 16 (a % 8) .. + 15 of q and k (two 16-byte
+// loads each); the 8 threads of a token sum with lane butterflies
+struct AuxQK {
+    u32x4 q[2], k[2];
+};
+template <class C, typename TI>
+__device__ __forceinline__ void aux_load_qk(AuxQK &x, const TI *__restrict__ q,
+                                            const TI *__restrict__ k, int64_t tok_base, int ntok,
+                                            int H, int h, int a)
+{
+    const int rowk = H * C::DK;
+    const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * 2);
+    const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * 2);
+    const int off = ((a >> 3) * rowk + h * C::DK + 16 * (a & 7)) * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        x.q[i] = bload128(rq, off + 16 * i);
+        x.k[i] = bload128(rk, off + 16 * i);
+    }
+}
+template <class C>
+__device__ __forceinline__ void aux_norms(Buf<C> &B, const AuxQK &x, int a)
+{
+    float nq = 0.f, nk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float q0 = __uint_as_float(x.q[i][e] << 16), q1 = __uint_as_float(x.q[i][e] & 0xffff0000u);
+            const float k0 = __uint_as_float(x.k[i][e] << 16), k1 = __uint_as_float(x.k[i][e] & 0xffff0000u);
+            nq = __builtin_fmaf(q0, q0, __builtin_fmaf(q1, q1, nq));
+            nk = __builtin_fmaf(k0, k0, __builtin_fmaf(k1, k1, nk));
+        }
+    nq = group_sum<8>(nq);
+    nk = group_sum<8>(nk);
+    if ((a & 7) == 0) {
+        B.NRM[0][0][a >> 3] = nq;
+        B.NRM[1][0][a >> 3] = nk;
+    }
+}
 template <class C>
 __device__ __forceinline__ void aux_kh(Buf<C> &B, int a)
 {
@@ -515,16 +556,22 @@ void kda_prefill_kernel(const Params<TI, TO> p)
             const int a = tid - (NW + C::NBW + 2) * WAVE;
             constexpr int NR = 3;
             AuxV r[NR];
-            auto load = [&](AuxV &x, int cc) {
-                aux_load_v<C>(x, p.v, bos + 16 * (int64_t)cc, v_on ? ntok_of(cc) : 0, H, h, DV,
+            AuxQK rn[GATED ? NR : 1];
+            auto load = [&](int i, int cc) {
+                aux_load_v<C>(r[i], p.v, bos + 16 * (int64_t)cc, v_on ? ntok_of(cc) : 0, H, h, DV,
                               col_base, a);
+                if constexpr (GATED) aux_load_qk<C>(rn[i], p.q, p.k, bos + 16 * (int64_t)cc, ntok_of(cc), H, h, a);
+            };
+            auto write = [&](Buf<C> &B, int i) {
+                aux_write_v<C>(B, r[i], a);
+                if constexpr (GATED) aux_norms<C>(B, rn[i], a);
             };
 #pragma unroll
-            for (int i = 0; i < NR; ++i) load(r[i], i);
-            if (nch > 0) aux_write_v<C>(sm.buf[0], r[0], a);
-            load(r[0], NR);
-            if (nch > 1) aux_write_v<C>(sm.buf[1], r[1], a);
-            load(r[1], NR + 1);
+            for (int i = 0; i < NR; ++i) load(i, i);
+            if (nch > 0) write(sm.buf[0], 0);
+            load(0, NR);
+            if (nch > 1) write(sm.buf[1], 1);
+            load(1, NR + 1);
             __syncthreads();
             if (nch > 0) aux_kh<C>(sm.buf[0], a);
             __syncthreads();
@@ -533,8 +580,8 @@ void kda_prefill_kernel(const Params<TI, TO> p)
             for (; c + NR <= nch; c += NR) {
 #pragma unroll
                 for (int i = 0; i < NR; ++i) {
-                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
-                    load(r[(i + 2) % NR], c + i + 2 + NR);
+                    if (c + i + 2 < nch) write(slot((c + i + 2) % 3), (i + 2) % NR);
+                    load((i + 2) % NR, c + i + 2 + NR);
                     if (c + i + 1 < nch) aux_kh<C>(slot((c + i + 1) % 3), a);
                     __syncthreads();
                 }
@@ -542,7 +589,7 @@ void kda_prefill_kernel(const Params<TI, TO> p)
 #pragma unroll
             for (int i = 0; i < NR - 1; ++i) {
                 if (c + i < nch) {
-                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
+                    if (c + i + 2 < nch) write(slot((c + i + 2) % 3), (i + 2) % NR);
                     if (c + i + 1 < nch) aux_kh<C>(slot((c + i + 1) % 3), a);
                     __syncthreads();
                 }
