@@ -79,7 +79,7 @@ def compare(got, ref, tol, tag):
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16),
-                                   (16, 128)])
+                                   (16, 128), (128, 64), (32, 32)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_bwd_shapes_ragged(dk, dv, dtype):
     """Packed lengths 1, 0, 17, 100, 16, 47: several chunks, ragged tails, a

@@ -70,7 +70,7 @@ def to_dev(d, dtype):
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16),
-                                   (16, 128)])
+                                   (16, 128), (128, 64)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_gated_shapes_ragged(dk, dv, dtype):
     """Ragged lengths (1, 0, 17, 100, 16, 47): the padded tokens of every

@@ -59,10 +59,11 @@ def test_tiny_fp32_reference_workload():
 
 # every (d_k, d_v) pair the library builds is covered between the shapes
 # here and the decode tests: narrow value blocks (d_v = 16, 32) with wide
-# keys, and the builder's two token-group layouts (four groups at d_k = 128,
-# eight below)
+# keys, the builder's two token-group layouts (four groups at d_k = 128,
+# eight below), and the auxiliary-wave configuration (bf16, d_k = 128,
+# d_v >= 64) with one and with two column blocks
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16), (16, 128),
-                                   (128, 32), (64, 16)])
+                                   (128, 32), (64, 16), (128, 64)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_shapes_ragged(dk, dv, dtype):
     """Several chunks, a ragged tail, T=1 and an empty sequence, with S0."""
