@@ -148,8 +148,10 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 const bf16x8 nk = s == 0 ? ah.nk : ld8b(&B.NK[j][kk]);
                 const bf16x8 qh = s == 0 ? ah.qh : ld8b(&B.QH[j][kk]);
                 const bf16x8 ql = s == 0 ? ah.ql : ld8b(&B.QL[j][kk]);
+                // -KE is a single bf16, so Sd's lo part would add nothing to
+                // X beyond KE's own rounding (checked in emulation against the
+                // oracle: o and S_T errors unchanged); only Sd hi enters X
                 x = mma32(nk, sh, x);
-                x = mma32(nk, sl, x);
                 // O^T = Sd^T QE^T: the state is the A operand, so each lane
                 // ends with four consecutive output columns of one token
                 o = mma32(sh, qh, o);            // the lo x lo term
