@@ -88,7 +88,7 @@ def stats(trace_dir, out_md, command):
     if not rows:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     lines = ["# rocprofv3 kernel statistics", "", "Command (from the repository root on the "
-             "GPU box):", "", "```", command, "```", "",
+             "GPU):", "", "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | share |",
              "|---|---|---|---|---|---|"]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
