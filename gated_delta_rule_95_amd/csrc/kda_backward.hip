@@ -645,6 +645,7 @@ void kda_bwd_sweep_mfma(const bwdm::SweepParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool is_cons = wave < NW;
     const bool is_build = !is_cons && wave < NW + C::NBW;
+    const bool is_aux = C::AUX && wave >= NW + C::NBW + 2;
     const int bw = wave - NW, btid = tid - C::NC;
     const int j = lane & 15, g4 = lane >> 4;
 
@@ -689,6 +690,42 @@ void kda_bwd_sweep_mfma(const bwdm::SweepParams p)
             if (c + i < nch) {
                 if (c + i + 2 < nch) build<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], bw, lane, btid, 1.f);
                 __syncthreads();
+            }
+        }
+    } else if (is_aux) {
+        if constexpr (C::AUX) {
+            // the dO block of step c + 2, on the builders' schedule
+            const int a = tid - (NW + C::NBW + 2) * WAVE;
+            constexpr int NR = 3;
+            AuxV r[NR];
+            auto load = [&](int i, int cc) {
+                aux_load_v<C>(r[i], p.dO, bos + 16 * (int64_t)chunk_of(cc), ntok_step(cc), H, h,
+                              DV, col_base, a);
+            };
+#pragma unroll
+            for (int i = 0; i < NR; ++i) load(i, i);
+            if (nch > 0) aux_write_v<C>(sm.buf[0], r[0], a);
+            load(0, NR);
+            if (nch > 1) aux_write_v<C>(sm.buf[1], r[1], a);
+            load(1, NR + 1);
+            __syncthreads();
+            __syncthreads();
+            int c = 0;
+#pragma unroll 1
+            for (; c + NR <= nch; c += NR) {
+#pragma unroll
+                for (int i = 0; i < NR; ++i) {
+                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
+                    load((i + 2) % NR, c + i + 2 + NR);
+                    __syncthreads();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NR - 1; ++i) {
+                if (c + i < nch) {
+                    if (c + i + 2 < nch) aux_write_v<C>(slot((c + i + 2) % 3), r[(i + 2) % NR], a);
+                    __syncthreads();
+                }
             }
         }
     } else if (!is_cons) {

@@ -174,11 +174,11 @@ struct Cfg {
     static constexpr int NBW = DK / 16 < 4 ? DK / 16 : 4;
     static constexpr int NBUF = NBUF_;             // LDS operand ring depth
     static constexpr int BV = 16 * NW;             // state columns per workgroup
-    // two auxiliary waves take the value block and the Kd^T rows off the
-    // builders (forward layouts, bf16, d_k = 128 with four consumers: with
+    // two auxiliary waves take the value block (and, in the forward, the
+    // Kd^T rows) off the builders (bf16, d_k = 128 with four consumers: with
     // them every SIMD holds one consumer, one builder and one helper or
     // auxiliary wave, three waves as before)
-    static constexpr bool AUX = BF && MODE_ == MODE_FWD && DK_ == 128 && NW_ == 4;
+    static constexpr bool AUX = BF && MODE_ != MODE_CHUNK && DK_ == 128 && NW_ == 4;
     static constexpr int NT = (NW + NBW + 2 + (AUX ? 2 : 0)) * WAVE;   // + 2 helpers
     static constexpr int NC = NW * WAVE;           // consumer threads
     static constexpr int NVT = 4 * BV;             // builder threads that move v (4 tokens each)
@@ -902,6 +902,97 @@ __device__ __forceinline__ int seq_of_rank(const int32_t *__restrict__ cu, int n
     const uint64_t m0 = __ballot(L0 >= 0 && k0 == r);
     const uint64_t m1 = __ballot(L1 >= 0 && k1 == r);
     return m0 ? __ffsll((unsigned long long)m0) - 1 : 64 + __ffsll((unsigned long long)m1) - 1;
+}
+
+// ---------------------------------------------------------------------------
+// auxiliary waves (Cfg::AUX): the value block of a chunk (v, or dO in the
+// sweep) and, in the forward, the Kd^T rows.  Aux thread a (0 .. 127) moves
+// columns 2 (a % (BV / 2)) and the next one, tokens 4 (a / (BV / 2)) .. + 3,
+// and writes the Kd^T row of channel a.
+// ---------------------------------------------------------------------------
+struct AuxV {
+    uint32_t w[4];                       // 4 tokens x 2 bf16 columns
+};
+template <class C, typename TI>
+__device__ __forceinline__ void aux_load_v(AuxV &x, const TI *__restrict__ v, int64_t tok_base,
+                                           int ntok, int H, int h, int DV, int col_base, int a)
+{
+    static_assert(C::BV == 64 && C::DK == 128 && C::BF, "aux mapping");
+    constexpr int CP = C::BV / 2;
+    const int cp = a % CP, tq = a / CP;
+    const int rowv = H * DV;
+    const rsrc_t rv = make_rsrc(v + tok_base * rowv, ntok * rowv * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x.w[i] = bload32(rv, ((4 * tq + i) * rowv + h * DV + col_base + 2 * cp) * 2);
+}
+template <class C>
+__device__ __forceinline__ void aux_write_v(Buf<C> &B, const AuxV &x, int a)
+{
+    constexpr int CP = C::BV / 2;
+    const int cp = a % CP, tq = a / CP;
+    // column 2 cp takes the low halves of the four token words, 2 cp + 1 the high
+    const uint32_t lo01 = __builtin_amdgcn_perm(x.w[1], x.w[0], 0x05040100u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(x.w[3], x.w[2], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(x.w[1], x.w[0], 0x07060302u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(x.w[3], x.w[2], 0x07060302u);
+    *reinterpret_cast<u32x2 *>(&B.VT[2 * cp][4 * tq]) = u32x2{lo01, lo23};
+    *reinterpret_cast<u32x2 *>(&B.VT[2 * cp + 1][4 * tq]) = u32x2{hi01, hi23};
+}
+// gated prologue: |q|^2 and |k|^2 of each token.  Aux thread a takes
+// token a / 8 and channels 16 (a % 8) .. + 15 of q and k (two 16-byte
+// loads each); the 8 threads of a token sum with lane butterflies
+struct AuxQK {
+    u32x4 q[2], k[2];
+};
+template <class C, typename TI>
+__device__ __forceinline__ void aux_load_qk(AuxQK &x, const TI *__restrict__ q,
+                                            const TI *__restrict__ k, int64_t tok_base, int ntok,
+                                            int H, int h, int a)
+{
+    const int rowk = H * C::DK;
+    const rsrc_t rq = make_rsrc(q + tok_base * rowk, ntok * rowk * 2);
+    const rsrc_t rk = make_rsrc(k + tok_base * rowk, ntok * rowk * 2);
+    const int off = ((a >> 3) * rowk + h * C::DK + 16 * (a & 7)) * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        x.q[i] = bload128(rq, off + 16 * i);
+        x.k[i] = bload128(rk, off + 16 * i);
+    }
+}
+template <class C>
+__device__ __forceinline__ void aux_norms(Buf<C> &B, const AuxQK &x, int a)
+{
+    float nq = 0.f, nk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float q0 = __uint_as_float(x.q[i][e] << 16), q1 = __uint_as_float(x.q[i][e] & 0xffff0000u);
+            const float k0 = __uint_as_float(x.k[i][e] << 16), k1 = __uint_as_float(x.k[i][e] & 0xffff0000u);
+            nq = __builtin_fmaf(q0, q0, __builtin_fmaf(q1, q1, nq));
+            nk = __builtin_fmaf(k0, k0, __builtin_fmaf(k1, k1, nk));
+        }
+    nq = group_sum<8>(nq);
+    nk = group_sum<8>(nk);
+    if ((a & 7) == 0) {
+        B.NRM[0][0][a >> 3] = nq;
+        B.NRM[1][0][a >> 3] = nk;
+    }
+}
+template <class C>
+__device__ __forceinline__ void aux_kh(Buf<C> &B, int a)
+{
+    const int kc = kpos<C>(a);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        bf16x8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = B.DH[4 * g + i][kc];
+            r[4 + i] = B.DL[4 * g + i][kc];
+        }
+        *reinterpret_cast<bf16x8 *>(&B.KH[a][8 * g]) = r;
+    }
 }
 
 }  // namespace kda
