@@ -29,6 +29,10 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_95_amd", "csrc")
 
 # MI355X: 256 compute units, 4 SIMDs each
 CU_NUM, SIMD_NUM = 256, 1024
+# GRBM_GUI_ACTIVE counts GPU cycles in each XCD's graphics block, and
+# rocprofv3 reports the sum over the XCDs of the chip (one row per dispatch):
+# the kernel's duration in cycles is that sum over XCD_NUM
+XCD_NUM = 8
 SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT",
                "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
                "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
@@ -158,20 +162,24 @@ def pmc(out_json, workload, copy_mib, commands, fetch_dir, write_dir, sq_dir=Non
             if cls == "copy":
                 continue
             gui = per["GRBM_GUI_ACTIVE"][cls]
+            cycles = gui / XCD_NUM if gui else None
             k = rec["kernels"].setdefault(cls, {"source_sha256_16": source_hash(cls)})
             raw = {name: per[name].get(cls) for name in SQ_COUNTERS}
             k["sq_raw"] = raw
             # rocprofv3's derived metrics: MfmaUtil, VALUBusy, LDSBankConflict
-            if gui:
-                k["mfma_busy_pct"] = 100.0 * (raw["SQ_VALU_MFMA_BUSY_CYCLES"] or 0) / (gui * SIMD_NUM)
-                k["valu_busy_pct"] = 100.0 * (raw["SQ_ACTIVE_INST_VALU"] or 0) / CU_NUM / gui
-                k["lds_bank_conflict_pct"] = 100.0 * (raw["SQ_LDS_BANK_CONFLICT"] or 0) / gui / CU_NUM
+            if cycles:
+                k["duration_cycles"] = cycles
+                k["mfma_busy_pct"] = 100.0 * (raw["SQ_VALU_MFMA_BUSY_CYCLES"] or 0) / (cycles * SIMD_NUM)
+                k["valu_busy_pct"] = 100.0 * (raw["SQ_ACTIVE_INST_VALU"] or 0) * 4 / SIMD_NUM / cycles
+                k["lds_bank_conflict_pct"] = 100.0 * (raw["SQ_LDS_BANK_CONFLICT"] or 0) / CU_NUM / cycles
             if raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] is not None:
                 k["mfma_bf16_flops"] = raw["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
         rec["sq_counters"] = SQ_COUNTERS
-        rec["sq_note"] = ("GRBM_GUI_ACTIVE and the SQ counters are summed over the "
-                          "instances rocprofv3 reports; the percentages use rocprofv3's "
-                          "MfmaUtil, VALUBusy and LDSBankConflict expressions with "
+        rec["sq_note"] = ("The SQ counters and GRBM_GUI_ACTIVE are chip-wide sums per "
+                          "dispatch; GRBM_GUI_ACTIVE sums the XCDs' cycle counts, so the "
+                          f"duration in cycles is it over XCD_NUM = {XCD_NUM}.  The "
+                          "percentages are rocprofv3's MfmaUtil, VALUBusy and "
+                          "LDSBankConflict expressions on that duration, with "
                           f"CU_NUM = {CU_NUM}, SIMD_NUM = {SIMD_NUM}")
     with open(out_json, "w") as f:
         json.dump(rec, f, indent=1)
