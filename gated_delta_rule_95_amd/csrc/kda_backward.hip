@@ -865,6 +865,41 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     const rsrc_t rv = make_rsrc(p.v + tok0 * H * DV, nt * vrow);
     const rsrc_t ro = make_rsrc(p.dO + tok0 * H * DV, nt * vrow);
 
+    // The column blocks (step 3) take the chunk-start state S and the exit
+    // cotangent L one block of 16 columns at a time, wave w taking blocks
+    // w, w + 4, ...  The first block's checkpoint tiles and v, dO values are
+    // requested before the operand build, so that their latency overlaps it;
+    // a later block's at its start, where the S-only products come first.
+    // (Holding a whole block ahead through the rounds of the previous one
+    // costs register spills at d_k = d_v = 128.)
+    constexpr int NCB = DV / 16, NIT = (NCB + 3) / 4;
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.Sck + (slot * H + h) * (int64_t)(DK * DV));
+    const f32x4 *cl = reinterpret_cast<const f32x4 *>(p.Lck + (slot * H + h) * (int64_t)(DK * DV));
+    f32x4 Sn[NT16], Ln[NT16];
+    u16x4 vbn, obn;                       // v, dO of column 16 cb + j, tokens 4 g4 + i
+    u32x2 o4n;                            // dO of token j, columns 16 cb + 4 g4 .. + 3
+    // checkpoints: read once, streamed
+    auto fetch_l = [&](int cb) {
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) Ln[t] = __builtin_nontemporal_load(&cl[(cb * NT16 + t) * WAVE + lane]);
+    };
+    auto fetch_s = [&](int cb) {
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) Sn[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int off = (4 * g4 + i) * vrow + (h * DV + 16 * cb + j) * 2;
+            vbn[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
+            obn[i] = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
+        }
+        o4n = bload64(ro, j * vrow + (h * DV + 16 * cb + 4 * g4) * 2);
+    };
+    if (wave < NCB) {
+        fetch_s(wave);
+        fetch_l(wave);
+    }
+
     // 1. chunk operands (builder waves); sums cleared
     if (wave < C::NBW) {
         Raw<C> r;
@@ -883,10 +918,11 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     // 3. blocks of 16 value columns, wave w taking blocks w, w + 4, ...  The
     // sums are split in four groups of channel tiles; in round r of an
     // iteration wave w adds its products into group (w + r) % 4 (and the
-    // wave of group 0 also adds dU X^T, dO U^T, that of group 1 the row sums
-    // of L o Sd), so no two waves touch the same sums between barriers
+    // wave of group 0 also adds dU X^T, dO U^T), so no two waves touch the
+    // same sums between barriers.  The row sums of L o Sd over the columns
+    // are the diagonal of L Sd^T, formed per channel tile from the same
+    // transposed tiles as the other sums.
     {
-        constexpr int NCB = DV / 16, NIT = (NCB + 3) / 4;
         constexpr int TPQ = NT16 >= 4 ? NT16 / 4 : 1;   // channel tiles per group
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const NegEye ne = neg_eye(lane);
@@ -901,50 +937,30 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         const bf16x8 t2h = cat(th4, th4), t2l = cat(tl4, tl4);
         const bf16x8 tth = ld8b(&B.TH[j][8 * g4]), ttl = ld8b(&B.TL[j][8 * g4]);
         const bf16x8 pth = ld8b(&B.PH[j][8 * g4]);
-        const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.Sck + (slot * H + h) * (int64_t)(DK * DV));
-        const f32x4 *cl = reinterpret_cast<const f32x4 *>(p.Lck + (slot * H + h) * (int64_t)(DK * DV));
-#pragma unroll 1
+        // (unrolled: the first block's tiles, fetched before the loop, are then
+        // not held across a back edge)
+#pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int cb = wave + 4 * it;
             const bool active = cb < NCB;                 // uniform over the wave
             bf16x8 sh[NS], sl[NS], lh[NS], ll[NS];
-            f32x4 GG[NT16], dT = zero, dP = zero;
+            f32x4 dT = zero, dP = zero;
             bf16x8 doo = {}, buh = {}, bul = {}, bxh = {}, bxl = {};
             if (active) {
-                f32x4 S[NT16], L[NT16];
-#pragma unroll
-                for (int t = 0; t < NT16; ++t) {       // checkpoints: read once, streamed
-                    S[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
-                    L[t] = __builtin_nontemporal_load(&cl[(cb * NT16 + t) * WAVE + lane]);
+                if (it > 0) {
+                    fetch_s(cb);
+                    fetch_l(cb);
                 }
-                const int col = 16 * cb + j;
-                // v and dO of column col, tokens 4 g4 + i; dO of token j,
-                // columns 16 cb + 4 g4 .. + 3
-                typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-                u16x4 vb, ob;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int off = (4 * g4 + i) * vrow + (h * DV + col) * 2;
-                    vb[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
-                    ob[i] = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
-                }
-                const bf16x4 v4 = __builtin_bit_cast(bf16x4, vb), d4 = __builtin_bit_cast(bf16x4, ob);
-                const bf16x4 o4 = __builtin_bit_cast(
-                    bf16x4, bload64(ro, j * vrow + (h * DV + 16 * cb + 4 * g4) * 2));
+                f32x4 S[NT16];
+                const bf16x4 v4 = __builtin_bit_cast(bf16x4, vbn), d4 = __builtin_bit_cast(bf16x4, obn);
+                const bf16x4 o4 = __builtin_bit_cast(bf16x4, o4n);
                 doo = cat(o4, o4);
-                // Sd, and the row sums of L o Sd over this block's columns
+                // Sd
 #pragma unroll
-                for (int t = 0; t < NT16; ++t) {
-                    S[t] *= *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
-                    GG[t] = L[t] * S[t];
+                for (int t = 0; t < NT16; ++t)
+                    S[t] = Sn[t] * *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) GG[t][e] = group_sum<16>(GG[t][e]);
-                }
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    split8(S[2 * s], S[2 * s + 1], ne, sh[s], sl[s]);
-                    split8(L[2 * s], L[2 * s + 1], ne, lh[s], ll[s]);
-                }
+                for (int s = 0; s < NS; ++s) split8(S[2 * s], S[2 * s + 1], ne, sh[s], sl[s]);
                 // X = V - KE Sd
                 f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
 #pragma unroll
@@ -959,6 +975,8 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                 // U = T X
                 f32x4 u = mma32(t2h, xhl, zero);
                 u = mma32(t2l, xhl, u);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) split8(Ln[2 * s], Ln[2 * s + 1], ne, lh[s], ll[s]);
                 // dU = P^T dO + Kd L
                 f32x4 du = mma32(pth, cat(d4, d4), zero);
 #pragma unroll
@@ -1010,6 +1028,10 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                             split4(mma32(shl, eye, zero), ne, sth, stl);   // Sd tile t transposed
                             split4(mma32(lhl, eye, zero), ne, lth, ltl);   // L tile t transposed
                             const bf16x8 sa = cat(sth, stl), la = cat(lth, ltl);
+                            // diag(L Sd^T): lane (n, g4) holds entry (4 g4 + e, n)
+                            f32x4 dd = mma32(la, cat(sth, sth), zero);
+                            dd = mma32(la, cat(stl, stl), dd);
+                            if ((j >> 2) == g4) sm.RG[16 * t + j] += dd[j & 3];
                             f32x4 y1 = sm.RED[0][t][lane], y2 = sm.RED[1][t][lane];
                             f32x4 kd = sm.RED[2][t][lane];
                             y1 = mma32(sa, doo, y1);                       // Sd dO^T
@@ -1025,15 +1047,30 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                     if (grp == 0) {
                         sm.RT[0][lane] += dT;
                         sm.RT[1][lane] += dP;
-                    } else if (grp == 1 && j == 0) {
-#pragma unroll
-                        for (int t = 0; t < NT16; ++t)
-                            *reinterpret_cast<f32x4 *>(&sm.RG[16 * t + 4 * g4]) += GG[t];
                     }
                 }
                 __syncthreads();
             }
         }
+    }
+    // the q, k values of step 5 (wave w takes channel tiles w, w + 4, ...),
+    // requested here so that they arrive during step 4
+    constexpr int NTW = (NT16 + 3) / 4;
+    uint16_t pq[NTW][4], pk[NTW][4];
+    u32x2 pq4[NTW], pk4[NTW];
+#pragma unroll
+    for (int w2 = 0; w2 < NTW; ++w2) {
+        const int t = wave + 4 * w2;
+        if (t >= NT16) break;              // uniform over the wave
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int off = (4 * st + g4) * krow + (h * DK + 16 * t + j) * 2;
+            pq[w2][st] = __builtin_amdgcn_raw_buffer_load_b16(rq, off, 0, 0);
+            pk[w2][st] = __builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, 0);
+        }
+        const int off = j * krow + (h * DK + 16 * t + 4 * g4) * 2;
+        pq4[w2] = bload64(rq, off);
+        pk4[w2] = bload64(rk, off);
     }
     // 4. through T = M Diag(beta) and A = strict_lower(Diag(beta) KE Kd^T)
     const int r16 = tid >> 4, i16 = tid & 15;
@@ -1075,15 +1112,17 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     // 5. dQE, dKE, dKd as [channel x token] tiles (fp32 matrix cores), then
     // dq, dk and the log-decay terms; QE, KE, Kd are re-formed from q, k and
     // the exponents
-    for (int t = wave; t < NT16; t += 4) {
+#pragma unroll
+    for (int w2 = 0; w2 < NTW; ++w2) {
+        const int t = wave + 4 * w2;
+        if (t >= NT16) break;              // uniform over the wave
         f32x4 q1 = {0.f, 0.f, 0.f, 0.f}, q2 = q1, q3 = q1;
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int kk = 4 * st + g4;                               // token index i
             const int ch = 16 * t + j;
-            const int off = kk * krow + (h * DK + ch) * 2;
-            const float qv = u16_to_f(__builtin_amdgcn_raw_buffer_load_b16(rq, off, 0, 0));
-            const float kv = u16_to_f(__builtin_amdgcn_raw_buffer_load_b16(rk, off, 0, 0));
+            const float qv = u16_to_f(pq[w2][st]);
+            const float kv = u16_to_f(pk[w2][st]);
             const float x = B.GX[kk][ch];
             const float E = fast_exp2(x), F = fast_exp2(-x);
             q1 = mma4(kv * F, sm.DP[j][kk], q1);                      // Kd^T dP^T
@@ -1091,9 +1130,8 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             q3 = mma4(qv * E, sm.DP[kk][j], q3);                      // QE^T dP
             q3 = mma4(kv * E, sm.DA[kk][j], q3);                      // + KE^T dA
         }
-        const int off = j * krow + (h * DK + 16 * t + 4 * g4) * 2;
-        const bf16x4 q4 = __builtin_bit_cast(bf16x4, bload64(rq, off));
-        const bf16x4 k4 = __builtin_bit_cast(bf16x4, bload64(rk, off));
+        const bf16x4 q4 = __builtin_bit_cast(bf16x4, pq4[w2]);
+        const bf16x4 k4 = __builtin_bit_cast(bf16x4, pk4[w2]);
         f32x4 dqv, dkv, gqv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
