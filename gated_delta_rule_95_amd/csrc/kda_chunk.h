@@ -25,15 +25,6 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// K = 16: lane (r, g) holds K slots 4 g .. 4 g + 3, the same contraction
-// index as the first four slots of each group in mma32 (the same matrix-pipe
-// time on gfx950, and no zero padding for four-slot operands)
-__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c)
-{
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -648,11 +639,12 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
 // the slots of group g; the left factor Y must then be given as Y^T in D
 // layout (lane (r, g) holds Y[r][4 g + i]).  So prod(YT, X) = Y X and
 // prod(X, YT) = X^T Y^T take the same two tiles with the roles swapped.
-// bf16: one K = 16 product.  fp32: four K = 4 steps.
+// bf16: one product, the K slots 4..7 of each group hold zeros.  fp32: four
+// K=4 steps.
 // ---------------------------------------------------------------------------
 template <bool BF> struct Tile;
 template <> struct Tile<true> {
-    bf16x4 v;                            // the four K slots of the lane's group
+    bf16x8 v;                            // [X (4 slots) | 0]
 };
 template <> struct Tile<false> {
     f32x4 x;
@@ -662,7 +654,7 @@ __device__ __forceinline__ Tile<BF> to_tile(f32x4 x)
 {
     if constexpr (BF) {
         const u32x2 h = {pack2(x[0], x[1]), pack2(x[2], x[3])};
-        return Tile<true>{__builtin_bit_cast(bf16x4, h)};
+        return Tile<true>{cat(__builtin_bit_cast(bf16x4, h), bf16x4{})};
     } else {
         return Tile<false>{x};
     }
@@ -672,7 +664,7 @@ __device__ __forceinline__ f32x4 prod(const Tile<BF> &yt, const Tile<BF> &x)
 {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     if constexpr (BF) {
-        return mma16(yt.v, x.v, zero);
+        return mma32(yt.v, x.v, zero);
     } else {
         f32x4 r = zero;
 #pragma unroll
