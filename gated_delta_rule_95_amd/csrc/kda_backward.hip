@@ -491,9 +491,11 @@ void kda_bwd_finish(const TI *__restrict__ q, const TI *__restrict__ k,
 // organisation: per (sequence, head, block of BV columns) one workgroup,
 // consumer waves holding L in the accumulator layout, builder waves forming
 // the operands of chunk c + 2 in a three-slot LDS ring (now in reverse chunk
-// order and with dO in place of v), two helper waves forming T^T and P^T of
-// chunk c + 1.  Per chunk it writes dV = dX and the exit cotangent L of the
-// chunk (in the 16 x 16 tiles of the state checkpoints); after chunk 0, dS0.
+// order and with dO in place of v; with d_k = 128 and four consumers two
+// auxiliary waves move the dO block, as they move v in the forward), two
+// helper waves forming T^T and P^T of chunk c + 1.  Per chunk it writes
+// dV = dX and the exit cotangent L of the chunk (in the 16 x 16 tiles of the
+// state checkpoints); after chunk 0, dS0.
 //
 // kda_bwd_chunk then takes every (chunk, head) independently: from the
 // chunk-start state S and the exit cotangent L it re-forms X, U, dU and dX
