@@ -44,6 +44,10 @@ def _load():
             h = lib.kda_oracle_head
             h.restype = None
             h.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 7
+            b = lib.kda_oracle_vjp
+            b.restype = ctypes.c_int
+            b.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 6 + \
+                [ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -87,3 +91,29 @@ def head(q, k, v, g, beta, S0=None, want_o: bool = True
     o = np.zeros((T, dv)) if want_o else None
     lib.kda_oracle_head(T, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S), _p(o))
     return o, S
+
+
+def vjp(q, k, v, g, beta, dO, cu_seqlens, S0=None, dST=None, threads: int = 0):
+    """Reverse-mode gradients of the packed varlen batch in fp64 (every
+    sequence independent, its own S0 and dS_T).  Shapes as in fwd(); dO
+    [N, H, dv]; dST [n_seqs, H, dk, dv] or None.  Returns dq, dk, dv, dg,
+    dbeta, dS0 (fp64) and the threads used.  Each thread keeps every state of
+    the longest sequence (T + 1 states of dk x dv doubles)."""
+    lib = _load()
+    q, k, v, g, beta, dO = (_f32(x) for x in (q, k, v, g, beta, dO))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    ns = len(cu) - 1
+    s0 = None if S0 is None else _f32(S0)
+    dst = None if dST is None else _f32(dST)
+    dq, dkk, dg = (np.zeros((N, H, dk)) for _ in range(3))
+    dvv = np.zeros((N, H, dv))
+    db = np.zeros((N, H))
+    dS0 = np.zeros((ns, H, dk, dv))
+    used = lib.kda_oracle_vjp(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(s0), _p(dO), _p(dst),
+                              _p(cu), ns, H, dk, dv, _p(dq), _p(dkk), _p(dvv), _p(dg), _p(db),
+                              _p(dS0), int(threads))
+    if used < 0:
+        raise MemoryError("kda_oracle_vjp: state buffer allocation failed")
+    return dq, dkk, dvv, dg, db, dS0, used

@@ -1,5 +1,6 @@
 """GPU parity of the chunked backward (kda_bwd_chunked) through the C ABI
-against the fp64 reverse-mode oracle (oracle/backward.py).
+against the fp64 reverse-mode oracle (oracle/backward.py; at full size its
+plain-C counterpart, oracle/kda_oracle.c).
 
 Every gradient (dq, dk, dv, dg, dbeta, dS0) is compared element by element:
 max |x - ref| / rms(ref) <= 1e-4 for fp32 inputs and 2e-2 for bf16 inputs
@@ -129,11 +130,12 @@ def test_bwd_rejects_small_workspace():
 
 
 @pytest.mark.timeout(600)
-def test_bwd_prefill_workload_sampled_chains():
+def test_bwd_prefill_workload_all_chains():
     """The prefill workload's shape (4 x 4096 tokens, H = 32, d = 128, bf16)
-    with random cotangents: every gradient finite, and five (sequence, head)
-    chains (each independent of the others) against the oracle."""
-    from oracle.backward import kda_recurrent_vjp
+    with random cotangents: every gradient of every (sequence, head) chain
+    against the plain-C fp64 oracle (OpenMP over chains), each chain's
+    errors taken against that chain's own scale."""
+    from oracle import clib
     from synth import WORKLOADS, batch_inputs
     wl = WORKLOADS["prefill"]
     b = batch_inputs(wl)
@@ -144,11 +146,18 @@ def test_bwd_prefill_workload_sampled_chains():
     got = run(b, dO, dST, torch.bfloat16, with_s0="s0" in b)
     for x in got:
         assert np.all(np.isfinite(x))
-    for s, h in ((0, 0), (1, 17), (2, 5), (3, 31), (ns - 1, H // 2)):
+    say("bwd prefill workload: C oracle")
+    ref = clib.vjp(b["q"], b["k"], b["v"], b["g"], b["beta"], dO, cu, b.get("s0"), dST,
+                   threads=16)[:6]
+    worst = {name: 0.0 for name in NAMES}
+    for s in range(ns):
         lo, hi = int(cu[s]), int(cu[s + 1])
-        sl = lambda x: x[lo:hi, h:h + 1]                   # noqa: E731
-        ref = kda_recurrent_vjp(sl(b["q"]), sl(b["k"]), sl(b["v"]), sl(b["g"]),
-                                sl(b["beta"]), sl(dO),
-                                b["s0"][s, h:h + 1] if "s0" in b else None, dST[s, h:h + 1])
-        mine = [sl(x) for x in got[:5]] + [got[5][s, h:h + 1]]
-        compare(mine, ref, 2e-2, f"chain ({s}, {h})")
+        for h in range(H):
+            sl = lambda x: x[lo:hi, h]                         # noqa: E731
+            mine = [sl(x) for x in got[:5]] + [got[5][s, h]]
+            want = [sl(x) for x in ref[:5]] + [ref[5][s, h]]
+            for name, x, y in zip(NAMES, mine, want):
+                worst[name] = max(worst[name], err(x, y))
+    say("  worst over the chains:", {k: f"{e:.2e}" for k, e in worst.items()})
+    bad = {k: e for k, e in worst.items() if not e <= 2e-2}
+    assert not bad, bad

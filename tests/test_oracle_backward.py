@@ -124,3 +124,64 @@ def test_planted_mistakes_fail_the_differences(name):
               - loss(dict(d, **{key: d[key] - eps * dirn}), cot)) / (2 * eps)
         worst = max(worst, abs(fd - float(np.sum(gr[key] * dirn))) / max(1.0, abs(fd)))
     assert worst > 1e-4, name
+
+
+# ---------------------------------------------------------------------------
+# The plain-C VJP (oracle/kda_oracle.c, kda_oracle_vjp): central differences
+# of the fp64 forward oracle at fp32-representable inputs (the C oracle reads
+# fp32), and agreement with the NumPy VJP on packed batches.
+# ---------------------------------------------------------------------------
+def _f32_exact(d):
+    return {key: np.asarray(x, np.float32).astype(np.float64) for key, x in d.items()}
+
+
+def c_grads(d, cot):
+    from oracle import clib
+    T, H, _ = d["q"].shape
+    r = clib.vjp(d["q"], d["k"], d["v"], d["g"], d["beta"], cot["dO"], np.array([0, T]),
+                 d["S0"][None], cot["dST"][None])
+    out = dict(zip(("q", "k", "v", "g", "beta"), r[:5]))
+    out["S0"] = r[5][0]
+    return out
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "S0"])
+@pytest.mark.parametrize("seed", [0, 7])
+def test_c_vjp_central_differences(name, seed):
+    d, cot = inputs(seed)
+    d, cot = _f32_exact(d), _f32_exact(cot)
+    gr = c_grads(d, cot)
+    r = np.random.default_rng(200 + seed)
+    for _ in range(3):
+        dirn = r.standard_normal(d[name].shape)
+        eps = 1e-6
+        dp = dict(d, **{name: d[name] + eps * dirn})
+        dm = dict(d, **{name: d[name] - eps * dirn})
+        fd = (loss(dp, cot) - loss(dm, cot)) / (2 * eps)
+        an = float(np.sum(gr[name] * dirn))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (name, fd, an)
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_c_vjp_matches_numpy_on_packed_batches(with_state):
+    from oracle import clib
+    r = np.random.default_rng(11)
+    cu = np.array([0, 1, 1, 17, 40, 41], np.int32)
+    N, H, dk, dv = 41, 3, 8, 12
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)   # noqa: E731
+    x = {"q": unit(r.standard_normal((N, H, dk))), "k": unit(r.standard_normal((N, H, dk))),
+         "v": r.standard_normal((N, H, dv)),
+         "g": -5.0 / (1.0 + np.exp(-r.standard_normal((N, H, dk)))),
+         "beta": 1.0 / (1.0 + np.exp(-r.standard_normal((N, H)))),
+         "dO": r.standard_normal((N, H, dv))}
+    x = _f32_exact(x)
+    S0 = dST = None
+    if with_state:
+        S0 = np.asarray(r.standard_normal((5, H, dk, dv)), np.float32).astype(np.float64)
+        dST = np.asarray(r.standard_normal((5, H, dk, dv)), np.float32).astype(np.float64)
+    a = clib.vjp(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], cu, S0, dST, threads=2)
+    b = bw.kda_recurrent_vjp_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], cu,
+                                    S0, dST)
+    for got, ref in zip(a[:6], b):
+        assert got.shape == ref.shape
+        assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, float(np.max(np.abs(ref))))
