@@ -155,8 +155,12 @@ def cpu_baseline(threads: int):
     dt1 = time.perf_counter() - t1
     one_core = wl.seqlen * 4 / wl.H / dt1
     host = host_cpu()
+    # fp64 work at the recurrence's 7 d^2 flops per token-head
+    flops = 7.0 * wl.dk * wl.dv * tokens * wl.H
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-            "one_core_value": one_core, "host": host,
+            "one_core_value": one_core, "fp64_gflops": flops / dt / 1e9,
+            "one_core_fp64_gflops": 7.0 * wl.dk * wl.dv * wl.seqlen * 4 / dt1 / 1e9,
+            "host": host,
             "sample": f"fp64 C oracle (token-by-token, OpenMP over (sequence, head)) on the "
                       f"whole prefill workload: {len(b['lengths'])} seqs x {wl.seqlen} tokens x "
                       f"{wl.H} heads, d=128; {dt:.2f} s wall on {used} threads "
@@ -221,6 +225,7 @@ def main():
     S0 = torch.from_numpy(b["s0"]).to(dev) if "s0" in b else None
     n_seqs = len(b["lengths"])
     tokens = int(b["cu_seqlens"][-1])
+    scan_depth = -(-int(max(b["lengths"])) // 16)     # sequential chunks of the longest chain
     equal = wl.seqlen is not None
     cu = None if equal else torch.from_numpy(b["cu_seqlens"]).to(dev)
     if equal:
@@ -386,7 +391,9 @@ def main():
                                f"d_k=d_v={wl.dk}, bf16 q/k/v/o, fp32 g/beta/state, "
                                f"S0={'given' if S0 is not None else 'zero'}, S_T returned",
                    "tokens": tokens, "n_seqs": n_seqs, "H": wl.H, "d_k": wl.dk, "d_v": wl.dv,
-                   "chunk": 16, "split_workspace_bytes": int(ws_bytes),
+                   "chunk": 16,
+                   "scan_depth": scan_depth,
+                   "split_workspace_bytes": int(ws_bytes),
                    "decode_workload": "256 seqs x 64 heads, d=128, fp32 state in place"
                    if dec else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -446,6 +453,8 @@ def main():
     if not args.no_cpu:
         threads = min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(threads)
+        if args.workload == "prefill":
+            out["cpu_baseline"]["gpu_speedup"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
 
 
