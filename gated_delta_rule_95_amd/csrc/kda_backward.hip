@@ -805,7 +805,7 @@ struct ChunkSmem {
     alignas(16) f32x4 RED[3][DK / 16][WAVE];
     alignas(16) f32x4 RT[2][WAVE];       // dU X^T, dO U^T (lane (i, g4): rows 4 g4 + e)
     alignas(16) float DT[16][17], DP[16][17], DM[16][17], W[16][17], DA[16][17];
-    alignas(16) float RG[DK];            // sum over the columns of L o Sd
+    alignas(16) float RG[4][DK];         // per wave: sum over its columns of L o Sd
     alignas(16) float GQ[DK];            // sum over the tokens of QE o (dO Sd^T) - KE o (dX Sd^T)
     alignas(16) float DB[16];
 };
@@ -910,7 +910,6 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     }
     for (int e = tid; e < 3 * NT16 * WAVE; e += 256) (&sm.RED[0][0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int e = tid; e < 2 * WAVE; e += 256) (&sm.RT[0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ch = tid; ch < DK; ch += 256) sm.RG[ch] = 0.f;
     __syncthreads();
     // 2. helpers: T^T, P^T, (I + A)^{-1} and KE Kd^T
     if (wave == 0) helper<C, 0>(B, lane);
@@ -918,12 +917,12 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     __syncthreads();
 
     // 3. blocks of 16 value columns, wave w taking blocks w, w + 4, ...  The
-    // sums are split in four groups of channel tiles; in round r of an
-    // iteration wave w adds its products into group (w + r) % 4 (and the
-    // wave of group 0 also adds dU X^T, dO U^T), so no two waves touch the
-    // same sums between barriers.  The row sums of L o Sd over the columns
-    // are the diagonal of L Sd^T, formed per channel tile from the same
-    // transposed tiles as the other sums.
+    // sums are split in four groups of channel tiles; in round r wave w adds
+    // the products of all its blocks into group (w + r) % 4 (and the wave of
+    // group 0 also adds dU X^T, dO U^T), so no two waves touch the same sums
+    // between barriers.  The row sums of L o Sd over the columns are the
+    // diagonal of L Sd^T, formed per channel tile from the same transposed
+    // tiles as the other sums and kept per lane until the column phase ends.
     {
         constexpr int TPQ = NT16 >= 4 ? NT16 / 4 : 1;   // channel tiles per group
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -939,120 +938,133 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         const bf16x8 t2h = cat(th4, th4), t2l = cat(tl4, tl4);
         const bf16x8 tth = ld8b(&B.TH[j][8 * g4]), ttl = ld8b(&B.TL[j][8 * g4]);
         const bf16x8 pth = ld8b(&B.PH[j][8 * g4]);
-        // (unrolled: the first block's tiles, fetched before the loop, are then
-        // not held across a back edge)
+        float DG[NT16];
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) DG[t] = 0.f;
+        // Every block of the wave first (the first block's tiles were fetched
+        // before the operand build, a later block's at its start), then four
+        // rounds over the channel groups, each taking the products of all the
+        // wave's blocks.  (Unrolled: the prefetched tiles are then not held
+        // across a back edge.)
+        bf16x8 sh[NIT][NS], sl[NIT][NS], lh[NIT][NS], ll[NIT][NS];
+        bf16x8 doo[NIT], buh[NIT], bul[NIT], bxh[NIT], bxl[NIT];
+        f32x4 dT = zero, dP = zero;                       // over the wave's blocks
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int cb = wave + 4 * it;
-            const bool active = cb < NCB;                 // uniform over the wave
-            bf16x8 sh[NS], sl[NS], lh[NS], ll[NS];
-            f32x4 dT = zero, dP = zero;
-            bf16x8 doo = {}, buh = {}, bul = {}, bxh = {}, bxl = {};
-            if (active) {
-                if (it > 0) {
-                    fetch_s(cb);
-                    fetch_l(cb);
-                }
-                f32x4 S[NT16];
-                const bf16x4 v4 = __builtin_bit_cast(bf16x4, vbn), d4 = __builtin_bit_cast(bf16x4, obn);
-                const bf16x4 o4 = __builtin_bit_cast(bf16x4, o4n);
-                doo = cat(o4, o4);
-                // Sd
-#pragma unroll
-                for (int t = 0; t < NT16; ++t)
-                    S[t] = Sn[t] * *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) split8(S[2 * s], S[2 * s + 1], ne, sh[s], sl[s]);
-                // X = V - KE Sd
-                f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const bf16x8 nk = ld8b(&B.NK[j][32 * s + 8 * g4]);
-                    x = mma32(nk, sh[s], x);
-                    x = mma32(nk, sl[s], x);
-                }
-                bf16x4 xh, xl;
-                split4(x, ne, xh, xl);
-                const bf16x8 xhl = cat(xh, xl);
-                // U = T X
-                f32x4 u = mma32(t2h, xhl, zero);
-                u = mma32(t2l, xhl, u);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) split8(Ln[2 * s], Ln[2 * s + 1], ne, lh[s], ll[s]);
-                // dU = P^T dO + Kd L
-                f32x4 du = mma32(pth, cat(d4, d4), zero);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const int kk = 32 * s + 8 * g4;
-                    const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
-                    du = mma32(dh, lh[s], du);
-                    du = mma32(dl, lh[s], du);
-                    du = mma32(dh, ll[s], du);
-                }
-                bf16x4 uh, ul, duh, dul;
-                split4(u, ne, uh, ul);
-                split4(du, ne, duh, dul);
-                const bf16x8 uhl = cat(uh, ul), duhl = cat(duh, dul);
-                // dX = T^T dU
-                f32x4 dx = mma32(tth, duhl, zero);
-                dx = mma32(ttl, duhl, dx);
-                bf16x4 dxh, dxl;
-                split4(dx, ne, dxh, dxl);
-                // transposed tiles (value columns as rows): lane (token n, g4)
-                // holds columns 16 cb + 4 g4 .. + 3 of token n
-                bf16x4 xth, xtl, uth, utl, duth, dutl, dxth, dxtl;
-                split4(mma32(xhl, eye, zero), ne, xth, xtl);
-                split4(mma32(uhl, eye, zero), ne, uth, utl);
-                split4(mma32(duhl, eye, zero), ne, duth, dutl);
-                split4(mma32(cat(dxh, dxl), eye, zero), ne, dxth, dxtl);
-                // dU X^T and dO U^T (16 x 16, lane (i, g4): rows 4 g4 + e)
-                dT = mma32(cat(duth, dutl), cat(xth, xth), zero);
-                dT = mma32(cat(duth, dutl), cat(xtl, xtl), dT);
-                dP = mma32(doo, cat(uth, utl), zero);
-                buh = cat(uth, uth); bul = cat(utl, utl);
-                bxh = cat(dxth, dxth); bxl = cat(dxtl, dxtl);
+            if (cb >= NCB) break;                         // uniform over the wave
+            if (it > 0) {
+                fetch_s(cb);
+                fetch_l(cb);
             }
+            f32x4 S[NT16];
+            const bf16x4 v4 = __builtin_bit_cast(bf16x4, vbn), d4 = __builtin_bit_cast(bf16x4, obn);
+            const bf16x4 o4 = __builtin_bit_cast(bf16x4, o4n);
+            doo[it] = cat(o4, o4);
+            // Sd
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int grp = (wave + r) & 3;
-                if (active) {
+            for (int t = 0; t < NT16; ++t)
+                S[t] = Sn[t] * *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 #pragma unroll
-                    for (int G = 0; G < 4; ++G) {
-                        if (G != grp || G * TPQ >= NT16) continue;
+            for (int s = 0; s < NS; ++s) split8(S[2 * s], S[2 * s + 1], ne, sh[it][s], sl[it][s]);
+            // X = V - KE Sd
+            f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
 #pragma unroll
-                        for (int tt = 0; tt < TPQ; ++tt) {
-                            const int t = G * TPQ + tt, s = t >> 1;
-                            const bf16x8 shl = (t & 1) ? cat(hi4(sh[s]), hi4(sl[s]))
-                                                       : cat(lo4(sh[s]), lo4(sl[s]));
-                            const bf16x8 lhl = (t & 1) ? cat(hi4(lh[s]), hi4(ll[s]))
-                                                       : cat(lo4(lh[s]), lo4(ll[s]));
-                            bf16x4 sth, stl, lth, ltl;
-                            split4(mma32(shl, eye, zero), ne, sth, stl);   // Sd tile t transposed
-                            split4(mma32(lhl, eye, zero), ne, lth, ltl);   // L tile t transposed
-                            const bf16x8 sa = cat(sth, stl), la = cat(lth, ltl);
-                            // diag(L Sd^T): lane (n, g4) holds entry (4 g4 + e, n)
+            for (int s = 0; s < NS; ++s) {
+                const bf16x8 nk = ld8b(&B.NK[j][32 * s + 8 * g4]);
+                x = mma32(nk, sh[it][s], x);
+                x = mma32(nk, sl[it][s], x);
+            }
+            bf16x4 xh, xl;
+            split4(x, ne, xh, xl);
+            const bf16x8 xhl = cat(xh, xl);
+            // U = T X
+            f32x4 u = mma32(t2h, xhl, zero);
+            u = mma32(t2l, xhl, u);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) split8(Ln[2 * s], Ln[2 * s + 1], ne, lh[it][s], ll[it][s]);
+            // dU = P^T dO + Kd L
+            f32x4 du = mma32(pth, cat(d4, d4), zero);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const int kk = 32 * s + 8 * g4;
+                const bf16x8 dh = ld8b(&B.DH[j][kk]), dl = ld8b(&B.DL[j][kk]);
+                du = mma32(dh, lh[it][s], du);
+                du = mma32(dl, lh[it][s], du);
+                du = mma32(dh, ll[it][s], du);
+            }
+            bf16x4 uh, ul, duh, dul;
+            split4(u, ne, uh, ul);
+            split4(du, ne, duh, dul);
+            const bf16x8 uhl = cat(uh, ul), duhl = cat(duh, dul);
+            // dX = T^T dU
+            f32x4 dx = mma32(tth, duhl, zero);
+            dx = mma32(ttl, duhl, dx);
+            bf16x4 dxh, dxl;
+            split4(dx, ne, dxh, dxl);
+            // transposed tiles (value columns as rows): lane (token n, g4)
+            // holds columns 16 cb + 4 g4 .. + 3 of token n
+            bf16x4 xth, xtl, uth, utl, duth, dutl, dxth, dxtl;
+            split4(mma32(xhl, eye, zero), ne, xth, xtl);
+            split4(mma32(uhl, eye, zero), ne, uth, utl);
+            split4(mma32(duhl, eye, zero), ne, duth, dutl);
+            split4(mma32(cat(dxh, dxl), eye, zero), ne, dxth, dxtl);
+            // dU X^T and dO U^T (16 x 16, lane (i, g4): rows 4 g4 + e)
+            dT = mma32(cat(duth, dutl), cat(xth, xth), dT);
+            dT = mma32(cat(duth, dutl), cat(xtl, xtl), dT);
+            dP = mma32(doo[it], cat(uth, utl), dP);
+            buh[it] = cat(uth, uth); bul[it] = cat(utl, utl);
+            bxh[it] = cat(dxth, dxth); bxl[it] = cat(dxtl, dxtl);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int grp = (wave + r) & 3;
+#pragma unroll
+            for (int G = 0; G < 4; ++G) {
+                if (G != grp || G * TPQ >= NT16 || wave >= NCB) continue;
+#pragma unroll
+                for (int tt = 0; tt < TPQ; ++tt) {
+                    const int t = G * TPQ + tt, s = t >> 1;
+                    f32x4 y1 = sm.RED[0][t][lane], y2 = sm.RED[1][t][lane];
+                    f32x4 kd = sm.RED[2][t][lane];
+#pragma unroll
+                    for (int it = 0; it < NIT; ++it) {
+                        if (wave + 4 * it >= NCB) break;   // uniform over the wave
+                        const bf16x8 shl = (t & 1) ? cat(hi4(sh[it][s]), hi4(sl[it][s]))
+                                                   : cat(lo4(sh[it][s]), lo4(sl[it][s]));
+                        const bf16x8 lhl = (t & 1) ? cat(hi4(lh[it][s]), hi4(ll[it][s]))
+                                                   : cat(lo4(lh[it][s]), lo4(ll[it][s]));
+                        bf16x4 sth, stl, lth, ltl;
+                        split4(mma32(shl, eye, zero), ne, sth, stl);   // Sd tile t transposed
+                        split4(mma32(lhl, eye, zero), ne, lth, ltl);   // L tile t transposed
+                        const bf16x8 sa = cat(sth, stl), la = cat(lth, ltl);
+                        // diag(L Sd^T): lane (n, g4) holds entry (4 g4 + e, n)
+                        {
                             f32x4 dd = mma32(la, cat(sth, sth), zero);
                             dd = mma32(la, cat(stl, stl), dd);
-                            if ((j >> 2) == g4) sm.RG[16 * t + j] += dd[j & 3];
-                            f32x4 y1 = sm.RED[0][t][lane], y2 = sm.RED[1][t][lane];
-                            f32x4 kd = sm.RED[2][t][lane];
-                            y1 = mma32(sa, doo, y1);                       // Sd dO^T
-                            y2 = mma32(sa, bxh, y2);                       // Sd dX^T
-                            y2 = mma32(sa, bxl, y2);
-                            kd = mma32(la, buh, kd);                       // L U^T
-                            kd = mma32(la, bul, kd);
-                            sm.RED[0][t][lane] = y1;
-                            sm.RED[1][t][lane] = y2;
-                            sm.RED[2][t][lane] = kd;
+                            const int e = j & 3;
+                            DG[t] += e == 0 ? dd[0] : e == 1 ? dd[1] : e == 2 ? dd[2] : dd[3];
                         }
+                        y1 = mma32(sa, doo[it], y1);                   // Sd dO^T
+                        y2 = mma32(sa, bxh[it], y2);                   // Sd dX^T
+                        y2 = mma32(sa, bxl[it], y2);
+                        kd = mma32(la, buh[it], kd);                   // L U^T
+                        kd = mma32(la, bul[it], kd);
                     }
-                    if (grp == 0) {
-                        sm.RT[0][lane] += dT;
-                        sm.RT[1][lane] += dP;
-                    }
+                    sm.RED[0][t][lane] = y1;
+                    sm.RED[1][t][lane] = y2;
+                    sm.RED[2][t][lane] = kd;
                 }
-                __syncthreads();
             }
+            if (grp == 0 && wave < NCB) {
+                sm.RT[0][lane] += dT;
+                sm.RT[1][lane] += dP;
+            }
+            __syncthreads();
+        }
+        if ((j >> 2) == g4) {
+#pragma unroll
+            for (int t = 0; t < NT16; ++t) sm.RG[wave][16 * t + j] = DG[t];
         }
     }
     // the q, k values of step 5 (wave w takes channel tiles w, w + 4, ...),
@@ -1168,7 +1180,7 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         float tot = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) tot += DXS[r][ch];
-        float acc = sm.RG[ch] + sm.GQ[ch] - tot + DXS[15][ch];
+        float acc = (sm.RG[0][ch] + sm.RG[1][ch]) + (sm.RG[2][ch] + sm.RG[3][ch]) + sm.GQ[ch] - tot + DXS[15][ch];
         for (int r = 15; r >= 0; --r) {
             if (r < 15) acc += DXS[r][ch];
             if (r < nt) p.dg[((tok0 + r) * H + h) * DK + ch] = acc;
