@@ -523,16 +523,23 @@ struct SweepParams {
 __device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
 __device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
 
-// B operand of the identity in the [4 hi | 4 lo] slot pairing: slot 8 kg + i
-// stands for row 4 kg + i % 4, so a product of a tile's [hi | lo] split (as
-// the A operand) with it is the transposed tile, hi + lo summed in fp32
-__device__ __forceinline__ bf16x8 eye8(int lane)
+// B operand of the identity on one half of the K slots: slot 8 kg + i
+// (i < 4 for half 0, i >= 4 for half 1) stands for row 4 kg + i % 4 and the
+// other half is zero, so a product of a 4 + 4 slot operand (as the A
+// operand) with it is the transposed tile of that half, exact in fp32
+__device__ __forceinline__ bf16x8 eye_half(int lane, int half)
 {
     const int n = lane & 15, kg = lane >> 4;
     bf16x8 e;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = (4 * kg + (i & 3) == n) ? (bf16)1.0f : (bf16)0.0f;
+    for (int i = 0; i < 8; ++i)
+        e[i] = ((i >> 2) == half && 4 * kg + (i & 3) == n) ? (bf16)1.0f : (bf16)0.0f;
     return e;
+}
+// four exact bf16 values held in fp32
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x)
+{
+    return __builtin_bit_cast(bf16x4, u32x2{pack2(x[0], x[1]), pack2(x[2], x[3])});
 }
 
 // operands of chunk c + 1 that its builders have finished, read before the
@@ -927,7 +934,11 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         constexpr int TPQ = NT16 >= 4 ? NT16 / 4 : 1;   // channel tiles per group
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const NegEye ne = neg_eye(lane);
-        const bf16x8 eye = eye8(lane);
+        const bf16x8 eyeA = eye_half(lane, 0), eyeB = eye_half(lane, 1);
+        // lane (n, g4) keeps the diagonal entry of row n: element n % 4 of g4 = n / 4
+        const int e3 = j & 3;
+        const float m0 = e3 == 0 ? 1.f : 0.f, m1 = e3 == 1 ? 1.f : 0.f;
+        const float m2 = e3 == 2 ? 1.f : 0.f, m3 = e3 == 3 ? 1.f : 0.f;
         // T rows [Th | Th], [Tl | Tl] read out of the T^T rows
         bf16x4 th4, tl4;
 #pragma unroll
@@ -1005,10 +1016,15 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             // transposed tiles (value columns as rows): lane (token n, g4)
             // holds columns 16 cb + 4 g4 .. + 3 of token n
             bf16x4 xth, xtl, uth, utl, duth, dutl, dxth, dxtl;
-            split4(mma32(xhl, eye, zero), ne, xth, xtl);
-            split4(mma32(uhl, eye, zero), ne, uth, utl);
-            split4(mma32(duhl, eye, zero), ne, duth, dutl);
-            split4(mma32(cat(dxh, dxl), eye, zero), ne, dxth, dxtl);
+            const bf16x8 dxhl = cat(dxh, dxl);
+            xth = to_bf16x4(mma32(xhl, eyeA, zero));
+            xtl = to_bf16x4(mma32(xhl, eyeB, zero));
+            uth = to_bf16x4(mma32(uhl, eyeA, zero));
+            utl = to_bf16x4(mma32(uhl, eyeB, zero));
+            duth = to_bf16x4(mma32(duhl, eyeA, zero));
+            dutl = to_bf16x4(mma32(duhl, eyeB, zero));
+            dxth = to_bf16x4(mma32(dxhl, eyeA, zero));
+            dxtl = to_bf16x4(mma32(dxhl, eyeB, zero));
             // dU X^T and dO U^T (16 x 16, lane (i, g4): rows 4 g4 + e)
             dT = mma32(cat(duth, dutl), cat(xth, xth), dT);
             dT = mma32(cat(duth, dutl), cat(xtl, xtl), dT);
@@ -1027,24 +1043,21 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                     const int t = G * TPQ + tt, s = t >> 1;
                     f32x4 y1 = sm.RED[0][t][lane], y2 = sm.RED[1][t][lane];
                     f32x4 kd = sm.RED[2][t][lane];
+                    f32x4 dd = zero;
+                    // tile t is half t % 2 of the [tile 2s | tile 2s + 1] operands
+                    const bf16x8 ey = (t & 1) ? eyeB : eyeA;
 #pragma unroll
                     for (int it = 0; it < NIT; ++it) {
                         if (wave + 4 * it >= NCB) break;   // uniform over the wave
-                        const bf16x8 shl = (t & 1) ? cat(hi4(sh[it][s]), hi4(sl[it][s]))
-                                                   : cat(lo4(sh[it][s]), lo4(sl[it][s]));
-                        const bf16x8 lhl = (t & 1) ? cat(hi4(lh[it][s]), hi4(ll[it][s]))
-                                                   : cat(lo4(lh[it][s]), lo4(ll[it][s]));
-                        bf16x4 sth, stl, lth, ltl;
-                        split4(mma32(shl, eye, zero), ne, sth, stl);   // Sd tile t transposed
-                        split4(mma32(lhl, eye, zero), ne, lth, ltl);   // L tile t transposed
+                        // Sd and L tile t transposed, hi and lo parts
+                        const bf16x4 sth = to_bf16x4(mma32(sh[it][s], ey, zero));
+                        const bf16x4 stl = to_bf16x4(mma32(sl[it][s], ey, zero));
+                        const bf16x4 lth = to_bf16x4(mma32(lh[it][s], ey, zero));
+                        const bf16x4 ltl = to_bf16x4(mma32(ll[it][s], ey, zero));
                         const bf16x8 sa = cat(sth, stl), la = cat(lth, ltl);
-                        // diag(L Sd^T): lane (n, g4) holds entry (4 g4 + e, n)
-                        {
-                            f32x4 dd = mma32(la, cat(sth, sth), zero);
-                            dd = mma32(la, cat(stl, stl), dd);
-                            const int e = j & 3;
-                            DG[t] += e == 0 ? dd[0] : e == 1 ? dd[1] : e == 2 ? dd[2] : dd[3];
-                        }
+                        // diag(L Sd^T): lane (n, g4) holds entries (4 g4 + e, n)
+                        dd = mma32(la, cat(sth, sth), dd);
+                        dd = mma32(la, cat(stl, stl), dd);
                         y1 = mma32(sa, doo[it], y1);                   // Sd dO^T
                         y2 = mma32(sa, bxh[it], y2);                   // Sd dX^T
                         y2 = mma32(sa, bxl[it], y2);
@@ -1054,6 +1067,7 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                     sm.RED[0][t][lane] = y1;
                     sm.RED[1][t][lane] = y2;
                     sm.RED[2][t][lane] = kd;
+                    DG[t] += (dd[0] * m0 + dd[1] * m1) + (dd[2] * m2 + dd[3] * m3);
                 }
             }
             if (grp == 0 && wave < NCB) {
