@@ -893,9 +893,8 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
 #pragma unroll
         for (int t = 0; t < NT16; ++t) Ln[t] = __builtin_nontemporal_load(&cl[(cb * NT16 + t) * WAVE + lane]);
     };
+    // (v and dO first: their 16-bit halves are packed as soon as they arrive)
     auto fetch_s = [&](int cb) {
-#pragma unroll
-        for (int t = 0; t < NT16; ++t) Sn[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * g4 + i) * vrow + (h * DV + 16 * cb + j) * 2;
@@ -903,18 +902,20 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             obn[i] = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
         }
         o4n = bload64(ro, j * vrow + (h * DV + 16 * cb + 4 * g4) * 2);
+#pragma unroll
+        for (int t = 0; t < NT16; ++t) Sn[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
     };
-    if (wave < NCB) {
+    // 1. chunk operands (builder waves); sums cleared.  The builders' raw
+    // inputs are requested before the checkpoint tiles: loads complete in
+    // order, so the build then waits only for its own inputs.
+    Raw<C> r;
+    if (wave < C::NBW)
+        load_raw<C>(r, p.q, p.k, p.v, p.g, p.beta, tok0, nt, 0, H, h, DV, 0, wave, lane, tid);
+    if (NCB >= 4 || wave < NCB) {
         fetch_s(wave);
         fetch_l(wave);
     }
-
-    // 1. chunk operands (builder waves); sums cleared
-    if (wave < C::NBW) {
-        Raw<C> r;
-        load_raw<C>(r, p.q, p.k, p.v, p.g, p.beta, tok0, nt, 0, H, h, DV, 0, wave, lane, tid);
-        build<C>(B, r, wave, lane, tid, 1.f);
-    }
+    if (wave < C::NBW) build<C>(B, r, wave, lane, tid, 1.f);
     for (int e = tid; e < 3 * NT16 * WAVE; e += 256) (&sm.RED[0][0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int e = tid; e < 2 * WAVE; e += 256) (&sm.RT[0][0])[e] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();

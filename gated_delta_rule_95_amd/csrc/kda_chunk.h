@@ -240,7 +240,7 @@ struct alignas(16) Buf {
     alignas(16) OT TL[C::LO ? 16 : 1][C::LDP];       // T lo
     alignas(16) OT PH[16][C::LDP];                   // P (hi); sweep: P^T as [4 hi | 4 lo]
     alignas(16) OT PL[C::LO && !C::BWD ? 16 : 1][C::LDP];   // P lo
-    alignas(16) OT VT[C::BV][C::LVT];                // value block, transposed  [column][token]
+    alignas(16) OT VT[C::CHUNK ? 1 : C::BV][C::LVT]; // value block, transposed  [column][token]
     alignas(16) float DEC[C::DK];                    // e^{Gc_16} per channel
     alignas(16) float BETA[16];
     // gated prologue: per builder wave, the partial sums of q^2 and k^2 of
@@ -341,6 +341,7 @@ __device__ __forceinline__ void load_raw(Raw<C> &r, const TI *__restrict__ q,
     // of column c (a wave's loads of one token are consecutive columns); the
     // condition is uniform over each wave and absent when all builders move v
     if constexpr (C::AUX) return;                  // the auxiliary waves move v
+    if constexpr (C::CHUNK) return;                // the chunk kernel reads v itself
     if (!C::all_v(tid)) return;
     const int c = tid % C::BV, tq = tid / C::BV;
     const int ev = 4 * tq * rowv + h * DV + col_base + c;
@@ -616,7 +617,7 @@ __device__ __forceinline__ void build(Buf<C> &B, const Raw<C> &r, int wave, int 
         // v is stored in its input type (the raw bits): four tokens of one
         // column per thread, one 8- or 16-byte write
         const int c = tid % C::BV, tq = tid / C::BV;
-        if (!C::AUX && C::all_v(tid)) {
+        if (!C::AUX && !C::CHUNK && C::all_v(tid)) {
             if constexpr (C::BF) *reinterpret_cast<u32x2 *>(&B.VT[c][4 * tq]) = r.v;
             else *reinterpret_cast<u32x4 *>(&B.VT[c][4 * tq]) = r.v;
         }
