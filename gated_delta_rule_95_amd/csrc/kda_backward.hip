@@ -878,9 +878,8 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     // cotangent L one block of 16 columns at a time, wave w taking blocks
     // w, w + 4, ...  The first block's checkpoint tiles and v, dO values are
     // requested before the operand build, so that their latency overlaps it;
-    // a later block's at its start, where the S-only products come first.
-    // (Holding a whole block ahead through the rounds of the previous one
-    // costs register spills at d_k = d_v = 128.)
+    // a later block's S (L) tiles as soon as the previous block's S (L) tiles
+    // have been split, into the same registers.
     constexpr int NCB = DV / 16, NIT = (NCB + 3) / 4;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.Sck + (slot * H + h) * (int64_t)(DK * DV));
@@ -965,10 +964,9 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         for (int it = 0; it < NIT; ++it) {
             const int cb = wave + 4 * it;
             if (cb >= NCB) break;                         // uniform over the wave
-            if (it > 0) {
-                fetch_s(cb);
-                fetch_l(cb);
-            }
+            // the next block's S and L tiles are requested as soon as this
+            // block's have been split (into the same registers)
+            const bool more = it + 1 < NIT && cb + 4 < NCB;
             f32x4 S[NT16];
             const bf16x4 v4 = __builtin_bit_cast(bf16x4, vbn), d4 = __builtin_bit_cast(bf16x4, obn);
             const bf16x4 o4 = __builtin_bit_cast(bf16x4, o4n);
@@ -979,6 +977,7 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
                 S[t] = Sn[t] * *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
 #pragma unroll
             for (int s = 0; s < NS; ++s) split8(S[2 * s], S[2 * s + 1], ne, sh[it][s], sl[it][s]);
+            if (more) fetch_s(cb + 4);
             // X = V - KE Sd
             f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};
 #pragma unroll
@@ -995,6 +994,7 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             u = mma32(t2l, xhl, u);
 #pragma unroll
             for (int s = 0; s < NS; ++s) split8(Ln[2 * s], Ln[2 * s + 1], ne, lh[it][s], ll[it][s]);
+            if (more) fetch_l(cb + 4);
             // dU = P^T dO + Kd L
             f32x4 du = mma32(pth, cat(d4, d4), zero);
 #pragma unroll
