@@ -1161,22 +1161,25 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         }
         const bf16x4 q4 = __builtin_bit_cast(bf16x4, pq4[w2]);
         const bf16x4 k4 = __builtin_bit_cast(bf16x4, pk4[w2]);
-        f32x4 dqv, dkv, gqv;
+        // (read into registers first: the log-decay terms are written over
+        // LDS rows the compiler cannot tell apart from the sums)
+        const f32x4 Y1 = sm.RED[0][t][lane], Y2 = sm.RED[1][t][lane], KD = sm.RED[2][t][lane];
+        const f32x4 GXv = *reinterpret_cast<const f32x4 *>(&B.GX[j][16 * t + 4 * g4]);   // log2 units, >= 0
+        f32x4 dqv, dkv, gqv, dxv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int ch = 16 * t + 4 * g4 + e;
-            const float y1 = sm.RED[0][t][lane][e], y2 = sm.RED[1][t][lane][e];
+            const float y1 = Y1[e], y2 = Y2[e];
             const float dqe = y1 + q1[e];
             const float dke = -y2 + q2[e];
-            const float dkd = sm.RED[2][t][lane][e] + q3[e];
-            const float x = B.GX[j][ch];                              // log2 units, >= 0
-            const float E = fast_exp2(x), F = fast_exp2(-x);
+            const float dkd = KD[e] + q3[e];
+            const float E = fast_exp2(GXv[e]), F = fast_exp2(-GXv[e]);
             const float qe = (float)q4[e] * E, ke = (float)k4[e] * E, kd = (float)k4[e] * F;
             dqv[e] = dqe * E;
             dkv[e] = dke * E + dkd * F;
             gqv[e] = qe * y1 - ke * y2;
-            DXS[j][ch] = dqe * qe + dke * ke - dkd * kd;
+            dxv[e] = dqe * qe + dke * ke - dkd * kd;
         }
+        *reinterpret_cast<f32x4 *>(&DXS[j][16 * t + 4 * g4]) = dxv;
         if (j < nt) {
             const int64_t o = ((tok0 + j) * H + h) * DK + 16 * t + 4 * g4;
             *reinterpret_cast<f32x4 *>(p.dq + o) = dqv;
@@ -1191,14 +1194,25 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     // 6. dg: x_r = Gc_r - Gc_16 gives dGc_r = dx_r (r < 15) and the chunk
     // total dGc_16 = gamma dgamma - sum_{r < 15} dx_r; dg_s = sum_{r >= s} dGc_r,
     // with gamma dgamma = sum_j dSd o Sd = L o Sd + QE o (dO Sd^T) - KE o (dX Sd^T)
-    for (int ch = tid; ch < DK; ch += 256) {
-        float tot = 0.f;
+    // (every thread: 256 / d_k threads per channel, each storing 16 d_k / 256
+    // of the tokens)
+    {
+        constexpr int NPC = 256 / DK, TPT = 16 / NPC;
+        static_assert(NPC * DK == 256 && NPC * TPT == 16, "dg mapping");
+        const int ch = tid % DK, r0 = (tid / DK) * TPT;
+        float dx[16], tot = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tot += DXS[r][ch];
-        float acc = (sm.RG[0][ch] + sm.RG[1][ch]) + (sm.RG[2][ch] + sm.RG[3][ch]) + sm.GQ[ch] - tot + DXS[15][ch];
+        for (int r = 0; r < 16; ++r) {
+            dx[r] = DXS[r][ch];
+            tot += dx[r];
+        }
+        float acc = (sm.RG[0][ch] + sm.RG[1][ch]) + (sm.RG[2][ch] + sm.RG[3][ch]) + sm.GQ[ch] - tot + dx[15];
+        float *dgp = p.dg + ((tok0 + r0) * H + h) * DK + ch;
+        const int64_t step = (int64_t)H * DK;
+#pragma unroll
         for (int r = 15; r >= 0; --r) {
-            if (r < 15) acc += DXS[r][ch];
-            if (r < nt) p.dg[((tok0 + r) * H + h) * DK + ch] = acc;
+            if (r < 15) acc += dx[r];
+            if (r >= r0 && r < r0 + TPT && r < nt) dgp[(r - r0) * step] = acc;
         }
     }
     if (tid < nt) p.db[(tok0 + tid) * H + h] = sm.DB[tid];
