@@ -643,11 +643,15 @@ __global__ __launch_bounds__(256) void kda_seg_scan_kernel(const float *__restri
 // Formed as O^T = E_s^T R^T on the bf16 matrix cores with hi/lo pairs of
 // both operands (Eh Rh + El Rh + Eh Rl per 32-deep step; the dropped El Rl
 // is near 2^-16 relative), so each lane ends with four consecutive outputs
-// of one token.  One workgroup per (chain, segment, 256 tokens); E_s^T is
-// staged in LDS as bf16 hi and lo rows.
+// of one token.  One workgroup of eight waves per (chain, segment,
+// kCorrTile tokens); E_s^T is staged in LDS as bf16 hi and lo rows.  A wave
+// takes 16 tokens at a time and requests all of their R and o~ before its
+// products (eight waves, so that enough loads are in flight per unit).
 // ---------------------------------------------------------------------------
+constexpr int kCorrTile = 256;                  // tokens per correction workgroup
+static_assert(kCorrTile % 128 == 0, "eight waves of 16 tokens per step");
 template <typename TO, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_seg_correct_kernel(
+__global__ __launch_bounds__(512) void kda_seg_correct_kernel(
     TO *__restrict__ o, const float *__restrict__ o0, const float *__restrict__ rq,
     const float *__restrict__ entry, int32_t H, int32_t seqlen, int32_t len0, int32_t lenS,
     int32_t nseg, int32_t tiles)
@@ -666,13 +670,13 @@ __global__ __launch_bounds__(256) void kda_seg_correct_kernel(
     const int t0 = len0 + (seg - 1) * lenS;       // segment start inside the sequence
     int segT = seqlen - t0;
     segT = segT < lenS ? segT : lenS;
-    const int tb = 256 * tile;
+    const int tb = kCorrTile * tile;
     if (tb >= segT) return;
-    const int ntile = segT - tb < 256 ? segT - tb : 256;
+    const int ntile = segT - tb < kCorrTile ? segT - tb : kCorrTile;
 
     // E_s^T as hi/lo bf16: thread takes rows r, r + 1 of one column c
     const float *E = entry + ((int64_t)chain * (nseg - 1) + seg - 1) * DK * DV;
-    for (int e = threadIdx.x; e < DK * DV / 2; e += 256) {
+    for (int e = threadIdx.x; e < DK * DV / 2; e += 512) {
         const int c = e % DV, r = 2 * (e / DV);
         const float x0 = E[r * DV + c], x1 = E[(r + 1) * DV + c];
         const uint32_t hw = pack2(x0, x1);
@@ -689,47 +693,55 @@ __global__ __launch_bounds__(256) void kda_seg_correct_kernel(
     const int64_t aug0 = (int64_t)n * (seqlen - len0) + (t0 - len0) + tb;  // o~ / R row
     const int64_t tok0 = (int64_t)n * seqlen + t0 + tb;                     // o row
 #pragma unroll 1
-    for (int it = 0; it < 4; ++it) {
-        const int tt = 64 * it + 16 * wave;
+    for (int it = 0; it < kCorrTile / 128; ++it) {
+        const int tt = 128 * it + 16 * wave;
         if (tt >= ntile) break;
         const int nt = ntile - tt < 16 ? ntile - tt : 16;
         const rsrc_t rr = make_rsrc(rq + (aug0 + tt) * H * DK, nt * H * DK * 4);
         const rsrc_t r0 = make_rsrc(o0 + (aug0 + tt) * H * DV, nt * H * DV * 4);
         const rsrc_t ro = make_rsrc(o + (tok0 + tt) * H * DV, nt * H * DV * (int)sizeof(TO));
-        // B = R^T: lane (token nn, kg) holds R[nn][32 s + 8 kg .. + 7]
-        bf16x8 rh[DK / 32], rl[DK / 32];
+        // every load of the 16 tokens first: R (lane (token nn, kg) holds
+        // R[nn][32 s + 8 kg .. + 7], the B operand R^T) and o~ (lane (token
+        // nn, kg) accumulates O[nn][16 ct + 4 kg .. + 3])
+        f32x4 ra[DK / 32], rb[DK / 32], acc[DV / 16];
 #pragma unroll
         for (int s2 = 0; s2 < DK / 32; ++s2) {
             const int off = ((nn * H + h) * DK + 32 * s2 + 8 * kg) * 4;
-            const f32x4 a = __builtin_bit_cast(f32x4, bload128(rr, off));
-            const f32x4 b = __builtin_bit_cast(f32x4, bload128(rr, off + 16));
+            ra[s2] = __builtin_bit_cast(f32x4, bload128(rr, off));
+            rb[s2] = __builtin_bit_cast(f32x4, bload128(rr, off + 16));
+        }
+#pragma unroll
+        for (int ct = 0; ct < DV / 16; ++ct)
+            acc[ct] = __builtin_bit_cast(f32x4, bload128(r0, ((nn * H + h) * DV + 16 * ct + 4 * kg) * 4));
+        bf16x8 rh[DK / 32], rl[DK / 32];
+#pragma unroll
+        for (int s2 = 0; s2 < DK / 32; ++s2) {
+            const f32x4 a = ra[s2], b = rb[s2];
             const u32x4 hw = {pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]),
                               pack2(b[2], b[3])};
             rh[s2] = __builtin_bit_cast(bf16x8, hw);
-            f32x4 ra, rb;
+            f32x4 da, db;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                ra[i] = a[i] - (float)rh[s2][i];
-                rb[i] = b[i] - (float)rh[s2][4 + i];
+                da[i] = a[i] - (float)rh[s2][i];
+                db[i] = b[i] - (float)rh[s2][4 + i];
             }
-            const u32x4 lw = {pack2(ra[0], ra[1]), pack2(ra[2], ra[3]), pack2(rb[0], rb[1]),
-                              pack2(rb[2], rb[3])};
+            const u32x4 lw = {pack2(da[0], da[1]), pack2(da[2], da[3]), pack2(db[0], db[1]),
+                              pack2(db[2], db[3])};
             rl[s2] = __builtin_bit_cast(bf16x8, lw);
         }
-#pragma unroll 2
+#pragma unroll
         for (int ct = 0; ct < DV / 16; ++ct) {
-            // lane (token nn, kg) accumulates O[nn][16 ct + 4 kg .. + 3]
             const int ocol = (nn * H + h) * DV + 16 * ct + 4 * kg;
-            f32x4 acc = __builtin_bit_cast(f32x4, bload128(r0, ocol * 4));
 #pragma unroll
             for (int s2 = 0; s2 < DK / 32; ++s2) {
                 const bf16x8 ah = ld8b(&EH[16 * ct + nn][32 * s2 + 8 * kg]);
                 const bf16x8 al = ld8b(&EL[16 * ct + nn][32 * s2 + 8 * kg]);
-                acc = mma32(ah, rh[s2], acc);
-                acc = mma32(al, rh[s2], acc);
-                acc = mma32(ah, rl[s2], acc);
+                acc[ct] = mma32(ah, rh[s2], acc[ct]);
+                acc[ct] = mma32(al, rh[s2], acc[ct]);
+                acc[ct] = mma32(ah, rl[s2], acc[ct]);
             }
-            bstore4(ro, ocol * (int)sizeof(TO), acc, TO{});
+            bstore4(ro, ocol * (int)sizeof(TO), acc[ct], TO{});
         }
     }
 }
@@ -870,6 +882,8 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
     const int64_t chains8 = ((chains + 7) / 8) * 8;
     const int64_t grid = chains8 * (NB + (int64_t)(pl.nseg - 1) * NA);
     if (grid * C::NT >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // grid size limit
+    if (pl.nseg > 1 && chains * (pl.nseg - 1) * ((pl.lenS + kCorrTile - 1) / kCorrTile) * 512 >= ((int64_t)1 << 32))
+        return hipErrorInvalidValue;                                       // correction grid
     Params<TI, TO> p{};
     p.q = (const TI *)a.q; p.k = (const TI *)a.k; p.v = (const TI *)a.v;
     p.g = a.g; p.beta = a.beta; p.S0 = a.S0; p.cu_seqlens = a.cu_seqlens;
@@ -897,9 +911,9 @@ static hipError_t launch_t(const PrefillArgs &a, int64_t chains, const SplitPlan
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if constexpr (DK % 32 == 0) {
-        const int tiles = (pl.lenS + 255) / 256;
+        const int tiles = (pl.lenS + kCorrTile - 1) / kCorrTile;
         const int64_t g2 = chains * (pl.nseg - 1) * tiles;
-        hipLaunchKernelGGL((kda_seg_correct_kernel<TO, DK, DV>), dim3((unsigned)g2), dim3(256), 0,
+        hipLaunchKernelGGL((kda_seg_correct_kernel<TO, DK, DV>), dim3((unsigned)g2), dim3(512), 0,
                            st, (TO *)a.o, p.o0, p.rq, p.entry, a.H, a.seqlen, pl.len0, pl.lenS,
                            pl.nseg, tiles);
         e = hipGetLastError();
