@@ -102,7 +102,7 @@ __device__ __forceinline__ void spec_token(int tid, SpecSmem<DK, DV> &sm,
     const f32x4 vv = *reinterpret_cast<const f32x4 *>(vv_ + 4 * cb);
     if constexpr (Sh::CB == 32) {
         // the two 32-lane halves of a wave hold the same columns: one
-        // register swap adds them; one half wave adds the per-wave sums
+        // register swap adds them; then two waves add the per-wave sums
         const int w = tid / WAVE, l = tid % WAVE;
         f32x4 wk, wq;
 #pragma unroll
@@ -125,21 +125,52 @@ __device__ __forceinline__ void spec_token(int tid, SpecSmem<DK, DV> &sm,
             if (l == 0) sm.wkq[w] = klo + khi;
         }
         __syncthreads();
-        if (tid < 32) {
-            f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = {0.f, 0.f, 0.f, 0.f};
-            float kqt = 0.f;
+        // u from the k sums on wave 0 (its two halves each add half of the
+        // waves' partials, one register swap joins them); the output's sums
+        // on wave 1, whose output waits for u after the next barrier
+        constexpr int HW = Sh::NWV / 2;
+        static_assert(Sh::NWV % 2 == 0 && Sh::NWV >= 2, "two halves of the per-wave sums");
+        const int hh = l >> 5, c = l & 31;
+        if (w == 0) {
+            f32x4 ks = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < Sh::NWV; ++r) {
-                ks += sm.wk[r][tid];
-                if constexpr (WANT_O) {
-                    qs += sm.wq[r][tid];
-                    kqt += sm.wkq[r];
-                }
+            for (int r = 0; r < HW; ++r) ks += sm.wk[hh * HW + r][c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float lo, hi;
+                half_pair(ks[e], lo, hi);
+                ks[e] = lo + hi;
             }
-            const f32x4 uu = b * (vv - ks);
-            sm.u[tid] = uu;
-            if constexpr (WANT_O) Elem<TO>::st4(o + 4 * tid, qs + uu * kqt);
+            if (hh == 0) sm.u[c] = b * (vv - ks);
         }
+        f32x4 qs = {0.f, 0.f, 0.f, 0.f};
+        float kqt = 0.f;
+        if constexpr (WANT_O) {
+            if (w == 1) {
+#pragma unroll
+                for (int r = 0; r < HW; ++r) {
+                    qs += sm.wq[hh * HW + r][c];
+                    kqt += sm.wkq[hh * HW + r];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float lo, hi;
+                    half_pair(qs[e], lo, hi);
+                    qs[e] = lo + hi;
+                }
+                float lo, hi;
+                half_pair(kqt, lo, hi);
+                kqt = lo + hi;
+            }
+        }
+        __syncthreads();
+        if constexpr (WANT_O) {
+            if (w == 1 && hh == 0) Elem<TO>::st4(o + 4 * c, qs + sm.u[c] * kqt);
+        }
+        const f32x4 u = sm.u[cb];
+#pragma unroll
+        for (int p = 0; p < Sh::R; ++p) s[p] += kv[r0 + p * Sh::RP] * u;
+        return;
     } else {
         sm.pk[r0][cb] = pk;
         if constexpr (WANT_O) {
