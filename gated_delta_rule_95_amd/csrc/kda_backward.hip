@@ -1112,32 +1112,30 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         }
     }
     __syncthreads();
-    sm.DM[r16][i16] = sm.DT[r16][i16] * B.BETA[i16];                 // dM = dT Diag(beta)
-    __syncthreads();
     {
-        float w = 0.f;                                                // W = M^T dM
+        float w = 0.f;                                                // W = M^T dM,
 #pragma unroll
-        for (int q = 0; q < 16; ++q) w = __builtin_fmaf(B.MI[q][r16], sm.DM[q][i16], w);
-        sm.W[r16][i16] = w;
+        for (int q = 0; q < 16; ++q) w = __builtin_fmaf(B.MI[q][r16], sm.DT[q][i16], w);
+        sm.W[r16][i16] = w * B.BETA[i16];                             // dM = dT Diag(beta)
     }
     __syncthreads();
     {
         float a = 0.f;                                                // dA = -W M^T
 #pragma unroll
         for (int q = 0; q < 16; ++q) a = __builtin_fmaf(sm.W[r16][q], B.MI[i16][q], a);
-        sm.DA[r16][i16] = i16 < r16 ? -a : 0.f;
+        const float da = i16 < r16 ? -a : 0.f;
+        sm.DM[r16][i16] = da;                                         // dA itself, for dbeta
+        sm.DA[r16][i16] = da * B.BETA[r16];                           // Diag(beta) dA
+        if (i16 > r16) sm.DP[r16][i16] = 0.f;                         // P lower incl.
     }
     __syncthreads();
+    // dbeta (read after the barrier that ends step 5)
     if (tid < 16) {
         float b = 0.f;
         for (int q = 0; q < 16; ++q) b = __builtin_fmaf(sm.DT[q][tid], B.MI[q][tid], b);
-        for (int q = 0; q < 16; ++q) b = __builtin_fmaf(sm.DA[tid][q], B.KK[tid][q], b);
+        for (int q = 0; q < 16; ++q) b = __builtin_fmaf(sm.DM[tid][q], B.KK[tid][q], b);
         sm.DB[tid] = b;
     }
-    __syncthreads();
-    sm.DA[r16][i16] *= B.BETA[r16];                                   // Diag(beta) dA
-    if (i16 > r16) sm.DP[r16][i16] = 0.f;                             // P lower incl.
-    __syncthreads();
     // 5. dQE, dKE, dKd as [channel x token] tiles (fp32 matrix cores), then
     // dq, dk and the log-decay terms; QE, KE, Kd are re-formed from q, k and
     // the exponents
