@@ -33,7 +33,9 @@
 //    file): kda_bwd_sweep_mfma carries L through the chunks in reverse and
 //    writes dv, dS0 and every chunk's exit cotangent; kda_bwd_chunk then
 //    forms all of a chunk's remaining gradients from its checkpointed
-//    entry state and exit cotangent, every (chunk, head) in parallel.
+//    entry state (stored by the checkpointing forward as the decayed Sd in
+//    bf16 hi/lo operand form) and exit cotangent, every (chunk, head) in
+//    parallel.
 //  * fp32 inputs (the precision reference) and d_k = 16 (first half):
 //    kda_bwd_sweep runs one workgroup per (sequence, head, block of
 //    columns) backwards over the chunks and writes dv, dS0 and per-block
@@ -874,17 +876,19 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
     const rsrc_t rv = make_rsrc(p.v + tok0 * H * DV, nt * vrow);
     const rsrc_t ro = make_rsrc(p.dO + tok0 * H * DV, nt * vrow);
 
-    // The column blocks (step 3) take the chunk-start state S and the exit
-    // cotangent L one block of 16 columns at a time, wave w taking blocks
-    // w, w + 4, ...  The first block's checkpoint tiles and v, dO values are
-    // requested before the operand build, so that their latency overlaps it;
-    // a later block's S (L) tiles as soon as the previous block's S (L) tiles
-    // have been split, into the same registers.
+    // The column blocks (step 3) take the chunk-start state, as the decayed
+    // Sd hi / lo operands the checkpointing forward split and stored, and the
+    // exit cotangent L one block of 16 columns at a time, wave w taking
+    // blocks w, w + 4, ...  The first block's checkpoint tiles and v, dO
+    // values are requested before the operand build, so that their latency
+    // overlaps it; a later block's Sd (L) tiles as soon as the previous
+    // block's have been taken up (L: split), into the same registers.
     constexpr int NCB = DV / 16, NIT = (NCB + 3) / 4;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.Sck + (slot * H + h) * (int64_t)(DK * DV));
     const f32x4 *cl = reinterpret_cast<const f32x4 *>(p.Lck + (slot * H + h) * (int64_t)(DK * DV));
-    f32x4 Sn[NT16], Ln[NT16];
+    bf16x8 shn[NS], sln[NS];              // Sd hi / lo operands, as the forward wrote them
+    f32x4 Ln[NT16];
     u16x4 vbn, obn;                       // v, dO of column 16 cb + j, tokens 4 g4 + i
     u32x2 o4n;                            // dO of token j, columns 16 cb + 4 g4 .. + 3
     // checkpoints: read once, streamed
@@ -902,7 +906,12 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
         }
         o4n = bload64(ro, j * vrow + (h * DV + 16 * cb + 4 * g4) * 2);
 #pragma unroll
-        for (int t = 0; t < NT16; ++t) Sn[t] = __builtin_nontemporal_load(&cs[(cb * NT16 + t) * WAVE + lane]);
+        for (int s = 0; s < NS; ++s) {
+            shn[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(&cs[(cb * NT16 + 2 * s) * WAVE + lane])));
+            sln[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(&cs[(cb * NT16 + 2 * s + 1) * WAVE + lane])));
+        }
     };
     // 1. chunk operands (builder waves); sums cleared.  The builders' raw
     // inputs are requested before the checkpoint tiles: loads complete in
@@ -967,16 +976,15 @@ void kda_bwd_chunk(const bwdm::ChunkParams p)
             // the next block's S and L tiles are requested as soon as this
             // block's have been split (into the same registers)
             const bool more = it + 1 < NIT && cb + 4 < NCB;
-            f32x4 S[NT16];
             const bf16x4 v4 = __builtin_bit_cast(bf16x4, vbn), d4 = __builtin_bit_cast(bf16x4, obn);
             const bf16x4 o4 = __builtin_bit_cast(bf16x4, o4n);
             doo[it] = cat(o4, o4);
-            // Sd
+            // Sd hi / lo, as the checkpointing forward split it
 #pragma unroll
-            for (int t = 0; t < NT16; ++t)
-                S[t] = Sn[t] * *reinterpret_cast<const f32x4 *>(&B.DEC[16 * t + 4 * g4]);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) split8(S[2 * s], S[2 * s + 1], ne, sh[it][s], sl[it][s]);
+            for (int s = 0; s < NS; ++s) {
+                sh[it][s] = shn[s];
+                sl[it][s] = sln[s];
+            }
             if (more) fetch_s(cb + 4);
             // X = V - KE Sd
             f32x4 x = {(float)v4[0], (float)v4[1], (float)v4[2], (float)v4[3]};

@@ -97,11 +97,15 @@ __device__ __forceinline__ void read_ahead(const Buf<C> &B, Ahead<C> &a, int wav
 
 // ---------------------------------------------------------------------------
 // consumer wave: the S-dependent chain of one chunk; returns O transposed in
-// the D layout: lane (j, g4) holds O[token j][columns 4 g4 .. 4 g4 + 3]
+// the D layout: lane (j, g4) holds O[token j][columns 4 g4 .. 4 g4 + 3].
+// With CKS (the checkpointing forward, bf16, d_k >= 32) it also stores the
+// chunk's Sd hi/lo operands, 16 bytes per lane each, at cks[(2 s + {0, 1}) x
+// 64 lanes]: the backward's chunk kernel takes them as they are.
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool CKS = false>
 __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16],
-                                         const Ahead<C> &ah, int wave, int lane)
+                                         const Ahead<C> &ah, int wave, int lane,
+                                         u32x4 *cks = nullptr)
 {
     const int j = lane & 15, g4 = lane >> 4;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -143,6 +147,10 @@ __device__ __forceinline__ f32x4 consume(const Buf<C> &B, f32x4 (&S)[C::DK / 16]
                 }
                 bf16x8 sh, sl;
                 split8(S[2 * s], S[2 * s + 1], ne, sh, sl);
+                if constexpr (CKS) {          // read once, by the backward: streamed
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sh), &cks[(2 * s) * WAVE]);
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, sl), &cks[(2 * s + 1) * WAVE]);
+                }
                 // stored positions 32 s + 8 g4 .. + 7 hold exactly these channels
                 const int kk = 32 * s + 8 * g4;
                 const bf16x8 nk = s == 0 ? ah.nk : ld8b(&B.NK[j][kk]);
@@ -549,7 +557,10 @@ void kda_prefill_kernel(const Params<TI, TO> p)
         __syncthreads();
         Ahead<C> ah;
         read_ahead<C>(sm.buf[0], ah, wave, lane);
-        // checkpoint tiles of this wave's 16 columns, chunk 0 of the sequence
+        // checkpoint tiles of this wave's 16 columns, chunk 0 of the sequence:
+        // the entry state in fp32 tiles, or (bf16, d_k >= 32) the decayed
+        // entry state Sd as the consumer's bf16 hi/lo operands
+        constexpr bool CKS = CKPT && C::BF && DK >= 32;
         f32x4 *ck = nullptr;
         if constexpr (CKPT)
             ck = reinterpret_cast<f32x4 *>(p.ckpt + ((bos / 16 + n) * H + h) * (int64_t)(DK * DV)) +
@@ -557,12 +568,16 @@ void kda_prefill_kernel(const Params<TI, TO> p)
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
             store_o(c - 1);
-            if constexpr (CKPT) {
+            if constexpr (CKPT && !CKS) {
 #pragma unroll
                 for (int t = 0; t < DK / 16; ++t)   // read once, by the backward: streamed
                     __builtin_nontemporal_store(S[t], &ck[(int64_t)c * H * (DK * DV / 4) + t * WAVE]);
             }
-            ov = consume<C>(slot(c % 3), S, ah, wave, lane);
+            if constexpr (CKS)
+                ov = consume<C, true>(slot(c % 3), S, ah, wave, lane,
+                                      reinterpret_cast<u32x4 *>(ck + (int64_t)c * H * (DK * DV / 4)));
+            else
+                ov = consume<C>(slot(c % 3), S, ah, wave, lane);
             read_ahead<C>(slot((c + 1) % 3), ah, wave, lane);
             __syncthreads();
         }
