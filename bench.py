@@ -114,6 +114,19 @@ def attach_counters(roofline: dict, workload: str, kernel: str) -> dict:
     return roofline
 
 
+def attach_counters_sum(roofline: dict, workload: str, kernels) -> dict:
+    """traffic of a call made of several kernels: the sum of their HBM bytes
+    per dispatch, when every one of them has a current counter record (null
+    otherwise), and each kernel's own figure beside it."""
+    recs = [counter_record(workload, k) for k in kernels]
+    ok = all(r is not None and "hbm_bytes_per_dispatch" in r for r in recs)
+    roofline["traffic"] = sum(r["hbm_bytes_per_dispatch"] for r in recs) if ok else None
+    if ok:
+        roofline["traffic_by_kernel"] = {k: r["hbm_bytes_per_dispatch"]
+                                         for k, r in zip(kernels, recs)}
+    return roofline
+
+
 def host_cpu() -> dict:
     """What the host offers the oracle: logical CPUs, the CPUs this process
     may run on, and the CPU model."""
@@ -427,6 +440,8 @@ def main():
             "roofline": {"bound": "hbm", "achieved": bb / bw_s / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": bb / bw_s / 1e9 / HBM_PEAK_GBS,
                          "kernel": "kda_bwd_chunked (3 kernels)", "alg_bytes_per_launch": bb}}
+        attach_counters_sum(out["backward"]["roofline"], args.workload,
+                            ("prefill_ckpt", "bwd_sweep_mfma", "bwd_chunk"))
     if dec:
         dw = WORKLOADS["decode"]
         st_b, all_b = decode_bytes(dw.n_seqs, dw.H, dw.dk, dw.dv)

@@ -75,6 +75,16 @@ def test_counters_only_for_matching_source_workload_and_kernel(record):
     assert bench.counter_record("prefill", "prefill") is None
 
 
+def test_summed_counters_need_every_kernel(record):
+    record()
+    r = bench.attach_counters_sum({}, "prefill", ("prefill", "decode"))
+    assert r == {"traffic": 130.0, "traffic_by_kernel": {"prefill": 123.0, "decode": 7.0}}
+    # one kernel without a current record leaves the sum unknown
+    assert bench.attach_counters_sum({}, "prefill", ("prefill", "spec")) == {"traffic": None}
+    record(prefill_hash="0" * 16)
+    assert bench.attach_counters_sum({}, "prefill", ("prefill", "decode")) == {"traffic": None}
+
+
 def test_counters_missing_record(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
     assert bench.counter_record("prefill", "prefill") is None
