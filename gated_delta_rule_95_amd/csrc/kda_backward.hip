@@ -500,12 +500,14 @@ void kda_bwd_finish(const TI *__restrict__ q, const TI *__restrict__ k,
 // state checkpoints); after chunk 0, dS0.
 //
 // kda_bwd_chunk then takes every (chunk, head) independently: from the
-// chunk-start state S and the exit cotangent L it re-forms X, U, dU and dX
+// chunk-start state (checkpointed as the decayed Sd in bf16 hi/lo operand
+// form) and the exit cotangent L it re-forms X, U, dU and dX
 // one block of 16 value columns at a time and accumulates the products that
 // contract over the value columns (dO Sd^T, dX Sd^T, L U^T, dU X^T, dO U^T
 // and the row sums of L o Sd) on the matrix cores; the rest is 16 x 16 and
 // 16 x d_k algebra.  Tiles whose contraction runs along the value columns
-// are transposed on the matrix core (a product with the identity).
+// are transposed on the matrix core (a product with the identity on one
+// half of the K slots, separately for the hi and the lo part).
 // ===========================================================================
 namespace bwdm {
 
