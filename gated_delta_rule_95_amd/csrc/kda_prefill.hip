@@ -278,10 +278,15 @@ struct Params {
     const TI *z, *braw;
     const float *A_log;
     // checkpointing variant (backward support): the state at the start of
-    // every chunk c of sequence n goes to slot bos / 16 + n + c of ckpt, as
-    // [slot][H][d_v / 16][d_k / 16][64][4] floats: per 16 x 16 tile (key rows
-    // 16 t .., value columns 16 cb ..), lane j + 16 g of the tile holds rows
-    // 16 t + 4 g .. + 3 of column 16 cb + j; o is not written
+    // every chunk c of sequence n goes to slot bos / 16 + n + c of ckpt, 64
+    // KiB per slot and head at d = 128; o is not written.  fp32 inputs or
+    // d_k = 16: [slot][H][d_v / 16][d_k / 16][64][4] floats, per 16 x 16 tile
+    // (key rows 16 t .., value columns 16 cb ..) lane j + 16 g holds rows
+    // 16 t + 4 g .. + 3 of column 16 cb + j.  bf16 with d_k >= 32: the
+    // decayed state Sd = Diag(e^{Gc_16}) S as the consumer's operands,
+    // [slot][H][d_v / 16][d_k / 32][hi, lo][64][16 bytes], lane j + 16 g of
+    // step s holding channels 32 s + 4 g .. + 3 and 32 s + 16 + 4 g .. + 3 of
+    // column 16 cb + j
     float *ckpt;
 };
 
